@@ -1,0 +1,16 @@
+"""CPU oracle for the sampled-softmax cross-entropy step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import anything from here. The HIP library never calls it, and the oracle shares
+no code with the HIP sources: the two meet only through the seeded input
+generator, which holds none of the method's arithmetic.
+
+* ``candidates``: the candidate build, sequential plain C (``candidates.c``).
+* ``ce``: loss and gradients in float64 numpy, dense for small shapes and
+  entry-by-entry ("sampled") for full-size shapes.
+
+Every function states the passage of the pages it follows. Parity pins live in
+``tests/test_oracle_*.py``; functions without an independent pin say so.
+"""
+from .candidates import build_candidates, OracleError  # noqa: F401
+from . import ce  # noqa: F401
