@@ -1,0 +1,176 @@
+/*
+ * sampled_ce.h -- C ABI of libsampledce.so: the sampled-softmax cross-entropy
+ * LM-head step (forward and backward) on AMD Instinct MI355X (gfx950).
+ *
+ * The method ("sampled_softmax.py", modded-nanogpt track_1_short, module
+ * docstring): for one microbatch of T tokens with hidden states x [T, d], the
+ * training cross-entropy is a softmax over a candidate set C of P classes that
+ * every token shares, instead of over all V classes. C holds every class that is
+ * a target somewhere in the microbatch plus negatives taken from the next window
+ * of the sweep k * stride mod V (stride coprime to V, so the sweep is a
+ * permutation). Logits are x @ W[C]^T; every target and prefix target is replaced
+ * by its position in C, and a prefix target that is not in C becomes -1, a label
+ * that contributes nothing. The gradient of W (the LM head, [V, d]) is dense, with
+ * zeros outside C. P = 0 means the full softmax over all V classes.
+ *
+ * Conventions shared by every entry point:
+ *   - Every array pointer is a DEVICE pointer unless its comment says "host".
+ *     The caller owns every buffer; the library never allocates or frees memory.
+ *   - Matrices are row-major and densely packed (row stride = row length).
+ *   - `dtype` is SCE_BF16 (bfloat16 storage, fp32 accumulation) or SCE_F32.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting for it. Nothing is synchronised and no
+ *     host<->device copy is made inside a call.
+ *   - Errors the host can see are returned synchronously and nothing is enqueued.
+ *     Errors only the device can see (a label out of range, more distinct targets
+ *     than P) are OR-ed into aux_out[3] (SCE_DEV_* bits); the other outputs of
+ *     such a call are unspecified but every access stays in bounds.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Calls that share a workspace must not overlap in time (use one workspace per
+ *     stream). Calls with distinct workspaces and outputs are independent.
+ */
+#ifndef SAMPLED_CE_H
+#define SAMPLED_CE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SCE_API __attribute__((visibility("default")))
+#else
+#define SCE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sce_status {
+  SCE_OK = 0,
+  SCE_EINVAL = 1,     /* an argument is out of range or a required pointer is NULL */
+  SCE_EWORKSPACE = 2, /* workspace NULL or smaller than sce_workspace_size() */
+  SCE_EHIP = 3        /* a HIP launch failed (see hipGetLastError) */
+} sce_status;
+
+typedef enum sce_dtype { SCE_F32 = 0, SCE_BF16 = 1 } sce_dtype;
+
+/* Device-detected conditions (bits of aux_out[3]). */
+#define SCE_DEV_TOO_MANY_TARGETS 1 /* distinct targets > P (the page asserts this never happens) */
+#define SCE_DEV_LABEL_RANGE 2      /* a target or prefix target outside [-1, V) */
+
+/* Limits checked on the host. */
+#define SCE_MAX_V_SAMPLED 131072 /* V limit when P > 0 (two candidate bitmaps held in LDS) */
+#define SCE_MAX_D 16384
+
+/*
+ * sce_workspace_size -- bytes of device workspace a call with these sizes needs.
+ * `bytes` is a HOST pointer. The largest piece is the [T, P] logits buffer
+ * (reused in place for its gradient): T * round_up(P or V, 8) elements of dtype.
+ * Returns SCE_EINVAL for sizes the call would reject.
+ */
+SCE_API sce_status sce_workspace_size(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, size_t* bytes);
+
+/*
+ * sce_build_candidates -- the candidate build alone ("sampled_softmax.py",
+ * CandidateBuilder.build and CandidateBuilder._negatives):
+ *   1. mark every class that is a target (-1 = no label, ignored);
+ *   2. need = P - (distinct targets); when need > 0 walk the window of the sweep
+ *      c_k = (k * stride) mod V for k = offset, offset+1, ... (wrapping mod V) of
+ *      length draw = min(V, floor(1.7 * need) + 256), and take the first `need`
+ *      classes that are not targets, in window order. If the window holds fewer,
+ *      take instead every s-th class (ascending) among the classes that are not
+ *      targets, s = max(1, free_count div need), the first `need` of them;
+ *   3. C = the marked classes in ascending order (exactly P of them);
+ *   4. target_pos[t] / prefix_pos[t] = the position in C of the label, -1 when the
+ *      label is -1 or (prefix only) not in C. Prefix targets never enter C.
+ *
+ *   targets        [T] int64: class id or -1.
+ *   prefix_targets [T] int64 or NULL (= every token has no prefix target).
+ *   P              1..V (P = 0 is not a candidate build and is rejected here).
+ *   stride         gcd(stride mod V, V) must be 1.
+ *   offset         sweep index where the window starts; any int64, taken mod V.
+ *   candidates_out [P] int32, ascending.   vocab_pos_out [V] int32 or NULL.
+ *   target_pos_out [T] int32.              prefix_pos_out [T] int32 or NULL.
+ *   aux_out        [4] int64 or NULL: {distinct targets, N = labels with
+ *                  position >= 0, next offset = (offset + draw) mod V or offset
+ *                  when need = 0, SCE_DEV_* bits}.
+ * Needs a workspace of at least sce_workspace_size(T, 8, V, P, SCE_F32) bytes
+ * (any size query with the same T, V, P is enough).
+ */
+SCE_API sce_status sce_build_candidates(const int64_t* targets, const int64_t* prefix_targets, int64_t T,
+                                int64_t V, int64_t P, int64_t stride, int64_t offset,
+                                int32_t* candidates_out, int32_t* vocab_pos_out,
+                                int32_t* target_pos_out, int32_t* prefix_pos_out,
+                                int64_t* aux_out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * sampled_ce_forward_backward -- the whole step: candidate build (as above),
+ * gather W_C = W[C], logits Z = x W_C^T (fp32 accumulation, stored in dtype),
+ * per row the log-sum-exp L_t = max_j Z + ln sum_j exp(Z - max), the loss
+ *     loss = (1/N) sum_t ( [y'_t >= 0](L_t - Z[t,y'_t]) + [p'_t >= 0](L_t - Z[t,p'_t]) ),
+ * with N = the number of labels whose position is >= 0 (targets plus surviving
+ * prefix targets; loss = 0 and all gradients 0 when N = 0), the logit gradient
+ *     dZ[t,j] = (n_t softmax(Z_t)_j - [j = y'_t] - [j = p'_t]) / N,  n_t = labels of row t,
+ * written in place over Z, then dX = dZ W_C and dW_C = dZ^T x, and the dense
+ * dW [V, d] = dW_C scattered to the rows of C, exactly zero elsewhere.
+ * (Softmax and its gradient: "Learning Triton one kernel at a time: softmax",
+ * definition, max subtraction, online softmax and backward sections; the
+ * normaliser N counts non-ignored labels as in "16_optimization_checks.py",
+ * lm_gradient.) P = 0 runs the same chain over all V classes with no candidate
+ * build, gather or scatter; P = V gives bit-identical results to P = 0.
+ *
+ *   x [T, d], W [V, d]            dtype, d a multiple of 8.
+ *   targets, prefix_targets       as in sce_build_candidates.
+ *   loss [1] float32.
+ *   dX [T, d], dW [V, d]          dtype, overwritten.
+ *   candidates_out [P] int32 or NULL; target_pos_out, prefix_pos_out [T] int32 or NULL.
+ *   row_lse_out [T] float32 or NULL: L_t.  row_loss_out [T] float32 or NULL: the
+ *   row's loss terms before division by N.
+ *   aux_out [4] int64 or NULL: as in sce_build_candidates (for P = 0: distinct
+ *   targets, N, offset mod V, SCE_DEV_* bits).
+ *   workspace: at least sce_workspace_size(T, d, V, P, dtype) bytes, 256-byte aligned.
+ * Inputs x, W, targets and prefix_targets are only read.
+ */
+SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64_t* targets,
+                                       const int64_t* prefix_targets, int64_t T, int64_t d,
+                                       int64_t V, int64_t P, int64_t stride, int64_t offset,
+                                       int dtype, float* loss, void* dX, void* dW,
+                                       int32_t* candidates_out, int32_t* target_pos_out,
+                                       int32_t* prefix_pos_out, float* row_lse_out,
+                                       float* row_loss_out, int64_t* aux_out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
+ * Stage timing for benchmarks. sce_profile_enable(1) makes every later call of
+ * sampled_ce_forward_backward record a HIP event on its stream at each stage
+ * boundary (up to 512 calls; later calls are not timed); sce_profile_enable(0)
+ * stops it. sce_profile_collect waits for the recorded events, writes into
+ * stage_ms (HOST array of at least SCE_NUM_STAGES doubles) the milliseconds each
+ * stage took summed over the timed calls, stores the number of calls in *ncalls
+ * (HOST, may be NULL) and forgets them. Process-wide state: not thread-safe.
+ */
+enum {
+  SCE_STAGE_CANDIDATES = 0, /* init, mark, build, remap */
+  SCE_STAGE_GATHER = 1,
+  SCE_STAGE_LOGITS = 2,
+  SCE_STAGE_CE = 3, /* CE forward/backward + loss reduction */
+  SCE_STAGE_DX = 4,
+  SCE_STAGE_DW = 5,
+  SCE_STAGE_SCATTER = 6,
+  SCE_NUM_STAGES = 7
+};
+SCE_API sce_status sce_profile_enable(int on);
+SCE_API sce_status sce_profile_collect(double* stage_ms, int nstages, int* ncalls);
+
+/* Human-readable name of an sce_status value (static string, never NULL). */
+SCE_API const char* sce_status_string(int status);
+
+/* ABI version of this header: 1. */
+SCE_API int sce_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAMPLED_CE_H */

@@ -1,0 +1,196 @@
+"""Thin ctypes binding of libsampledce.so (C ABI in include/sampled_ce.h).
+
+Argument marshalling only: tensors become device pointers, the current HIP
+stream is passed through, outputs are allocated with torch. Every step of the
+computation runs in the library's HIP kernels; there is no Python or CPU
+fallback, and a missing library raises.
+"""
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsampledce.so")
+
+SCE_F32, SCE_BF16 = 0, 1
+DEV_TOO_MANY_TARGETS, DEV_LABEL_RANGE = 1, 2
+STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
+
+EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sampled_ce_forward_backward",
+           "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
+STAGES = ("candidates", "gather", "logits", "ce", "dx", "dw", "scatter")
+
+_lib = None
+
+
+class SceError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}")
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsampledce.so (built by sampled_softmax_cross_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m sampled_softmax_cross_amd.build`; "
+            "there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.sce_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(sz)]
+    lib.sce_workspace_size.restype = i32
+    lib.sce_build_candidates.argtypes = [p, p, i64, i64, i64, i64, i64, p, p, p, p, p, p, sz, p]
+    lib.sce_build_candidates.restype = i32
+    lib.sampled_ce_forward_backward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
+                                                p, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.sampled_ce_forward_backward.restype = i32
+    lib.sce_status_string.argtypes = [i32]
+    lib.sce_status_string.restype = ctypes.c_char_p
+    lib.sce_profile_enable.argtypes = [i32]
+    lib.sce_profile_enable.restype = i32
+    lib.sce_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), i32, ctypes.POINTER(i32)]
+    lib.sce_profile_collect.restype = i32
+    lib.sce_abi_version.argtypes = []
+    lib.sce_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return SCE_BF16
+    if dt == torch.float32:
+        return SCE_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def workspace_size(T, d, V, P, dtype) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    rc = lib.sce_workspace_size(T, d, V, P, dtype_code(dtype) if isinstance(dtype, torch.dtype)
+                                else int(dtype), ctypes.byref(out))
+    if rc != 0:
+        raise SceError("sce_workspace_size", rc)
+    return out.value
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A reusable device workspace of at least nbytes (one per device and stream)."""
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        _ws_cache.pop(key, None)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def build_candidates(targets, prefix_targets, V, P, stride, offset, *, want_vocab_pos=False,
+                     ws=None):
+    """Device candidate build; returns dict of tensors (C, target_pos, prefix_pos,
+    vocab_pos or None, aux int64[4] = distinct, N, next_offset, device status)."""
+    lib = load_library()
+    dev = targets.device
+    T = targets.shape[0]
+    C = torch.empty(P, dtype=torch.int32, device=dev)
+    tpos = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    ppos = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    vpos = torch.empty(V, dtype=torch.int32, device=dev) if want_vocab_pos else None
+    aux = torch.empty(4, dtype=torch.int64, device=dev)
+    nbytes = workspace_size(T, 8, V, P, SCE_F32)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    rc = lib.sce_build_candidates(_ptr(targets), _ptr(prefix_targets), T, V, P, stride, offset,
+                                  _ptr(C), _ptr(vpos), _ptr(tpos), _ptr(ppos), _ptr(aux),
+                                  _ptr(ws), ws.numel(), _stream(dev))
+    if rc != 0:
+        raise SceError("sce_build_candidates", rc)
+    return dict(C=C, target_pos=tpos[:T], prefix_pos=ppos[:T], vocab_pos=vpos, aux=aux)
+
+
+def forward_backward(x, W, targets, prefix_targets, P, stride, offset, *, outputs=None, ws=None,
+                     want_rows=False):
+    """One sampled-CE step. x [T,d], W [V,d] (bf16 or fp32, contiguous, same dtype),
+    targets / prefix_targets int64 [T] (prefix may be None).
+
+    Returns dict: loss (fp32 [1]), dX, dW, C (int32 [P], ascending; None for P == 0),
+    target_pos, prefix_pos (int32 [T]), aux (int64 [4]), and with want_rows the
+    per-row log-sum-exp and loss terms (fp32 [T]). `outputs` may pass preallocated
+    tensors under the same keys.
+    """
+    lib = load_library()
+    dev = x.device
+    T, d = x.shape
+    V = W.shape[0]
+    if W.dtype != x.dtype or W.shape[1] != d:
+        raise ValueError("x and W must share dtype and hidden size")
+    for name, t in (("x", x), ("W", W), ("targets", targets)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if targets.dtype != torch.int64 or (prefix_targets is not None and prefix_targets.dtype != torch.int64):
+        raise ValueError("labels must be int64")
+    o = dict(outputs or {})
+    if "loss" not in o:
+        o["loss"] = torch.empty(1, dtype=torch.float32, device=dev)
+    if "dX" not in o:
+        o["dX"] = torch.empty_like(x)
+    if "dW" not in o:
+        o["dW"] = torch.empty_like(W)
+    if "C" not in o:
+        o["C"] = torch.empty(max(P, 1), dtype=torch.int32, device=dev) if P > 0 else None
+    for k in ("target_pos", "prefix_pos"):
+        if k not in o:
+            o[k] = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    if "aux" not in o:
+        o["aux"] = torch.empty(4, dtype=torch.int64, device=dev)
+    if want_rows:
+        for k in ("row_lse", "row_loss"):
+            if k not in o:
+                o[k] = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+    dt = dtype_code(x.dtype)
+    nbytes = workspace_size(T, d, V, P, dt)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    rc = lib.sampled_ce_forward_backward(
+        _ptr(x), _ptr(W), _ptr(targets), _ptr(prefix_targets), T, d, V, P, stride, offset, dt,
+        _ptr(o["loss"]), _ptr(o["dX"]), _ptr(o["dW"]), _ptr(o["C"]), _ptr(o["target_pos"]),
+        _ptr(o["prefix_pos"]), _ptr(o.get("row_lse")), _ptr(o.get("row_loss")), _ptr(o["aux"]),
+        _ptr(ws), ws.numel(), _stream(dev))
+    if rc != 0:
+        raise SceError("sampled_ce_forward_backward", rc)
+    if o["C"] is not None:
+        o["C"] = o["C"][:P]
+    o["target_pos"] = o["target_pos"][:T]
+    o["prefix_pos"] = o["prefix_pos"][:T]
+    return o
+
+
+def profile_enable(on: bool) -> None:
+    """Start/stop per-stage HIP-event timing inside the library."""
+    load_library().sce_profile_enable(1 if on else 0)
+
+
+def profile_collect():
+    """(milliseconds per stage summed over the timed calls, number of calls)."""
+    lib = load_library()
+    arr = (ctypes.c_double * len(STAGES))()
+    n = ctypes.c_int(0)
+    rc = lib.sce_profile_collect(arr, len(STAGES), ctypes.byref(n))
+    if rc != 0:
+        raise SceError("sce_profile_collect", rc)
+    return {k: arr[i] for i, k in enumerate(STAGES)}, n.value

@@ -1,0 +1,259 @@
+// C ABI of libsampledce.so: argument checks, workspace layout and the launch
+// sequence of the step. Every launch goes to the caller's stream; nothing here
+// allocates, synchronises or copies between host and device.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/sampled_ce.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace sce {
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b != 0) {
+    const int64_t r = a % b;
+    a = b;
+    b = r;
+  }
+  return a < 0 ? -a : a;
+}
+int64_t mod64(int64_t a, int64_t m) {
+  const int64_t r = a % m;
+  return r < 0 ? r + m : r;
+}
+
+// Byte offsets of every workspace piece.
+struct Plan {
+  int64_t Peff = 0, ldz = 0;
+  int splits = 1;
+  size_t counters = 0, bytemap = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
+  size_t wc = 0, z = 0, part = 0, total = 0;
+};
+
+// full = false: only what the candidate build needs.
+Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full) {
+  Plan p;
+  const size_t es = dtype == SCE_BF16 ? 2 : 4;
+  p.Peff = P == 0 ? V : P;
+  p.ldz = round_up(p.Peff, 8);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  p.counters = take(kNumCounters * sizeof(int32_t));
+  p.bytemap = take((size_t)bytemap_bytes((int)V));
+  p.vocab_pos = take((size_t)V * sizeof(int32_t));
+  p.cand = take((size_t)(P > 0 ? P : 1) * sizeof(int32_t));
+  p.tpos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
+  p.ppos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
+  p.row_loss = take((size_t)(T > 0 ? T : 1) * sizeof(float));
+  if (full) {
+    p.wc = take(P > 0 ? (size_t)P * d * es : 0);
+    p.z = take((size_t)T * p.ldz * es);
+    p.splits = gemm_dw_splits(p.Peff, d, T);
+    p.part = take((size_t)p.splits * p.Peff * d * sizeof(float));
+  }
+  p.total = off;
+  return p;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+sce_status check_sizes(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool need_d) {
+  if (T < 0 || T > INT32_MAX / 2) return SCE_EINVAL;
+  if (V < 1 || V > INT32_MAX / 2) return SCE_EINVAL;
+  if (P < 0 || P > V) return SCE_EINVAL;
+  if (P > 0 && V > SCE_MAX_V_SAMPLED) return SCE_EINVAL;
+  if (need_d && (d < 8 || d % 8 != 0 || d > SCE_MAX_D)) return SCE_EINVAL;
+  if (dtype != SCE_F32 && dtype != SCE_BF16) return SCE_EINVAL;
+  return SCE_OK;
+}
+
+sce_status hip_status(hipError_t e) { return e == hipSuccess ? SCE_OK : SCE_EHIP; }
+
+// Optional stage timing: when enabled, every call records a HIP event on its
+// stream at each stage boundary; sce_profile_collect() sums the elapsed times.
+constexpr int kMaxProfiledCalls = 512;
+struct Profile {
+  bool on = false;
+  int calls = 0;
+  hipEvent_t ev[kMaxProfiledCalls][SCE_NUM_STAGES + 1] = {};
+  bool created[kMaxProfiledCalls] = {};
+} g_prof;
+
+struct StageMarks {
+  int call = -1;
+  hipStream_t s;
+  explicit StageMarks(hipStream_t stream) : s(stream) {
+    if (!g_prof.on || g_prof.calls >= kMaxProfiledCalls) return;
+    call = g_prof.calls++;
+    if (!g_prof.created[call]) {
+      for (int i = 0; i <= SCE_NUM_STAGES; ++i) (void)hipEventCreate(&g_prof.ev[call][i]);
+      g_prof.created[call] = true;
+    }
+  }
+  // Marks the boundary before stage `i` (i == SCE_NUM_STAGES: after the last).
+  void mark(int i) {
+    if (call >= 0) (void)hipEventRecord(g_prof.ev[call][i], s);
+  }
+};
+
+}  // namespace
+}  // namespace sce
+
+using namespace sce;
+
+extern "C" {
+
+int sce_abi_version(void) { return 1; }
+
+const char* sce_status_string(int status) {
+  switch (status) {
+    case SCE_OK: return "SCE_OK";
+    case SCE_EINVAL: return "SCE_EINVAL: invalid argument";
+    case SCE_EWORKSPACE: return "SCE_EWORKSPACE: workspace missing or too small";
+    case SCE_EHIP: return "SCE_EHIP: HIP launch failed";
+    default: return "unknown sce_status";
+  }
+}
+
+sce_status sce_workspace_size(int64_t T, int64_t d, int64_t V, int64_t P, int dtype,
+                              size_t* bytes) {
+  if (bytes == nullptr) return SCE_EINVAL;
+  const sce_status st = check_sizes(T, d, V, P, dtype, true);
+  if (st != SCE_OK) return st;
+  *bytes = make_plan(T, d, V, P, dtype, true).total;
+  return SCE_OK;
+}
+
+sce_status sce_build_candidates(const int64_t* targets, const int64_t* prefix_targets, int64_t T,
+                                int64_t V, int64_t P, int64_t stride, int64_t offset,
+                                int32_t* candidates_out, int32_t* vocab_pos_out,
+                                int32_t* target_pos_out, int32_t* prefix_pos_out,
+                                int64_t* aux_out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  sce_status st = check_sizes(T, 8, V, P, SCE_F32, false);
+  if (st != SCE_OK || P < 1) return SCE_EINVAL;
+  if ((T > 0 && (targets == nullptr || target_pos_out == nullptr)) || candidates_out == nullptr)
+    return SCE_EINVAL;
+  const int64_t s = mod64(stride, V);
+  if (gcd64(s, V) != 1) return SCE_EINVAL;
+  const Plan p = make_plan(T, 8, V, P, SCE_F32, false);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  int32_t* vocab_pos = vocab_pos_out ? vocab_pos_out : reinterpret_cast<int32_t*>(ws + p.vocab_pos);
+  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
+  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
+                                   (int)mod64(offset, V), reinterpret_cast<uint8_t*>(ws + p.bytemap),
+                                   counters, candidates_out, vocab_pos, target_pos_out, ppos, hs);
+  if (e == hipSuccess && aux_out) e = launch_write_aux(counters, aux_out, hs);
+  return hip_status(e);
+}
+
+sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64_t* targets,
+                                       const int64_t* prefix_targets, int64_t T, int64_t d,
+                                       int64_t V, int64_t P, int64_t stride, int64_t offset,
+                                       int dtype, float* loss, void* dX, void* dW,
+                                       int32_t* candidates_out, int32_t* target_pos_out,
+                                       int32_t* prefix_pos_out, float* row_lse_out,
+                                       float* row_loss_out, int64_t* aux_out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  sce_status st = check_sizes(T, d, V, P, dtype, true);
+  if (st != SCE_OK) return st;
+  if (W == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
+  if (T > 0 && (x == nullptr || targets == nullptr || dX == nullptr)) return SCE_EINVAL;
+  if ((x && !aligned16(x)) || !aligned16(W) || (dX && !aligned16(dX)) || !aligned16(dW))
+    return SCE_EINVAL;
+  int64_t s = 1;
+  if (P > 0) {
+    s = mod64(stride, V);
+    if (gcd64(s, V) != 1) return SCE_EINVAL;
+  }
+  const Plan p = make_plan(T, d, V, P, dtype, true);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+
+  const bool bf16 = dtype == SCE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  int32_t* vocab_pos = reinterpret_cast<int32_t*>(ws + p.vocab_pos);
+  int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
+  int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+  void* Z = ws + p.z;
+  float* part = reinterpret_cast<float*>(ws + p.part);
+  const void* WC = P > 0 ? static_cast<const void*>(ws + p.wc) : W;
+
+  StageMarks marks(hs);
+  marks.mark(SCE_STAGE_CANDIDATES);
+  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
+                                   (int)mod64(offset, V), reinterpret_cast<uint8_t*>(ws + p.bytemap),
+                                   counters, cand, vocab_pos, tpos, ppos, hs);
+  marks.mark(SCE_STAGE_GATHER);
+  if (e == hipSuccess && P > 0) e = launch_gather_rows(W, cand, (int)P, (int)(d * es), ws + p.wc, hs);
+  marks.mark(SCE_STAGE_LOGITS);
+  if (e == hipSuccess && T > 0) {
+    GemmArgs g{x, d, WC, d, Z, p.ldz, T, p.Peff, d, 1, 0};
+    e = launch_gemm(Gemm::Logits, bf16, g, hs);
+  }
+  marks.mark(SCE_STAGE_CE);
+  if (e == hipSuccess)
+    e = launch_ce_rows(Z, p.ldz, (int)T, (int)p.Peff, bf16, tpos, ppos, counters, row_loss,
+                       row_lse_out, hs);
+  if (e == hipSuccess) e = launch_finalize(row_loss, (int)T, counters, loss, aux_out, hs);
+  marks.mark(SCE_STAGE_DX);
+  if (e == hipSuccess && T > 0) {
+    GemmArgs g{Z, p.ldz, WC, d, dX, d, T, d, p.Peff, 1, 0};
+    e = launch_gemm(Gemm::DX, bf16, g, hs);
+  }
+  marks.mark(SCE_STAGE_DW);
+  if (e == hipSuccess) {
+    GemmArgs g{Z, p.ldz, x, d, part, d, p.Peff, d, T, p.splits, p.Peff * d};
+    e = launch_gemm(Gemm::DW, bf16, g, hs);
+  }
+  marks.mark(SCE_STAGE_SCATTER);
+  if (e == hipSuccess)
+    e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? vocab_pos : nullptr, (int)V,
+                            (int)d, bf16, dW, hs);
+  marks.mark(SCE_NUM_STAGES);
+  return hip_status(e);
+}
+
+sce_status sce_profile_enable(int on) {
+  if (on && !g_prof.on) g_prof.calls = 0;  // a new timing window; disabling keeps the record
+  g_prof.on = on != 0;
+  return SCE_OK;
+}
+
+sce_status sce_profile_collect(double* stage_ms, int nstages, int* ncalls) {
+  if (stage_ms == nullptr || nstages < SCE_NUM_STAGES) return SCE_EINVAL;
+  for (int i = 0; i < nstages; ++i) stage_ms[i] = 0.0;
+  for (int c = 0; c < g_prof.calls; ++c) {
+    if (hipEventSynchronize(g_prof.ev[c][SCE_NUM_STAGES]) != hipSuccess) return SCE_EHIP;
+    for (int i = 0; i < SCE_NUM_STAGES; ++i) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_prof.ev[c][i], g_prof.ev[c][i + 1]) != hipSuccess)
+        return SCE_EHIP;
+      stage_ms[i] += ms;
+    }
+  }
+  if (ncalls) *ncalls = g_prof.calls;
+  g_prof.calls = 0;
+  return SCE_OK;
+}
+
+}  // extern "C"

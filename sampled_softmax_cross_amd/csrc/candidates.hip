@@ -1,0 +1,252 @@
+// Candidate-set construction on the device ("sampled_softmax.py",
+// CandidateBuilder.build and CandidateBuilder._negatives):
+//   mark targets -> count distinct -> walk the stride window for negatives (or the
+//   page's fallback) -> ascending C and the class -> position map -> remap labels.
+//
+// The page builds C on the host with numpy; here the whole build is four small
+// kernels on the caller's stream, so the step needs no host round trip. The one
+// inherently sequential part (an ordered compaction of the window) runs in a
+// single 1024-lane workgroup with the candidate bitmap in LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace sce {
+
+// Zero the byte map (nbytes is a multiple of 16) and the counters.
+__global__ __launch_bounds__(256) void k_cand_init(uint4* __restrict__ bytemap, int nvec,
+                                                   int32_t* __restrict__ counters) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nvec) bytemap[i] = make_uint4(0, 0, 0, 0);
+  if (i < kNumCounters) counters[i] = 0;
+}
+
+// bytemap[y] = 1 for every target y >= 0; range check of targets and prefix targets.
+__global__ __launch_bounds__(256) void k_cand_mark(const int64_t* __restrict__ targets,
+                                                   const int64_t* __restrict__ prefix, int T,
+                                                   int V, uint8_t* __restrict__ bytemap,
+                                                   int32_t* __restrict__ counters) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int64_t y = targets[t];
+  bool bad = y < -1 || y >= V;
+  if (!bad && y >= 0) bytemap[y] = 1;  // racing stores all write 1
+  if (prefix != nullptr) {
+    const int64_t p = prefix[t];
+    bad |= p < -1 || p >= V;
+  }
+  if (bad) atomicOr(&counters[kStatus], kDevLabelRange);
+}
+
+// 16 bytes that are each 0 or 1 -> 16 bits.
+__device__ __forceinline__ uint32_t bytes_to_bits(uint4 q) {
+  auto four = [](uint32_t d) { return (d & 1u) | ((d >> 7) & 2u) | ((d >> 14) & 4u) | ((d >> 21) & 8u); };
+  return four(q.x) | (four(q.y) << 4) | (four(q.z) << 8) | (four(q.w) << 12);
+}
+
+__device__ __forceinline__ uint32_t valid_bits(int w, int V) {
+  const int rem = V - w * 32;
+  return rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
+}
+
+// One workgroup of kBuildThreads lanes. Dynamic LDS: 2 * ceil(V/32) words.
+// P == 0 only counts distinct targets (full softmax: no candidate set).
+__global__ __launch_bounds__(kBuildThreads) void k_cand_build(
+    const uint8_t* __restrict__ bytemap, int V, int P, int stride, int off,
+    int32_t* __restrict__ C, int32_t* __restrict__ vocab_pos, int32_t* __restrict__ counters) {
+  extern __shared__ uint32_t lds_words[];
+  __shared__ int scratch[kBuildThreads / kWave + 1];
+  const int W = (V + 31) >> 5;
+  uint32_t* mark = lds_words;      // candidate bitmap
+  uint32_t* aux = lds_words + W;   // window picks, then per-word prefix counts
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+
+  // 1. byte map -> bitmap; distinct targets.
+  int cnt = 0;
+  for (int w = tid; w < W; w += nt) {
+    const uint4* src = reinterpret_cast<const uint4*>(bytemap) + 2 * w;
+    const uint32_t bits = bytes_to_bits(src[0]) | (bytes_to_bits(src[1]) << 16);
+    if (P > 0) {  // P == 0 launches without LDS: counting only
+      mark[w] = bits;
+      aux[w] = 0;
+    }
+    cnt += __popc(bits);
+  }
+  const int distinct = block_sum_int(cnt, scratch);  // (contains barriers)
+  if (P == 0) {
+    if (tid == 0) {
+      counters[kDistinct] = distinct;
+      counters[kNextOffset] = off;
+    }
+    return;
+  }
+  if (distinct > P) {
+    // The page asserts this never happens. Flag it and leave a harmless map
+    // (C = [0, P)) so that every later kernel stays in bounds.
+    if (tid == 0) {
+      atomicOr(&counters[kStatus], kDevTooManyTargets);
+      counters[kDistinct] = distinct;
+      counters[kNextOffset] = off;
+    }
+    for (int i = tid; i < P; i += nt) C[i] = i;
+    for (int c = tid; c < V; c += nt) vocab_pos[c] = c < P ? c : -1;
+    return;
+  }
+
+  const int need = P - distinct;
+  int next_off = off;
+  if (need > 0) {
+    const int draw = min(V, (17 * need) / 10 + 256);  // == floor(1.7 * need) + 256
+    next_off = (int)(((int64_t)off + draw) % V);
+    // 2. Walk window positions i = 0 .. draw-1 (class ((off+i) mod V) * stride mod V)
+    //    in order; the first `need` free classes become negatives. Each lane takes
+    //    kWalk consecutive positions; a block scan orders the lanes.
+    constexpr int kWalk = 4;
+    int seen = 0;  // free classes met so far (block-uniform)
+    for (int base = 0; base < draw && seen < need; base += nt * kWalk) {
+      const int i0 = base + tid * kWalk;
+      int cls[kWalk];
+      uint32_t freemask = 0;
+      int c = 0;
+      if (i0 < draw) c = (int)(((int64_t)((off + i0) % V) * stride) % V);
+#pragma unroll
+      for (int j = 0; j < kWalk; ++j) {
+        cls[j] = c;
+        if (i0 + j < draw && !((mark[c >> 5] >> (c & 31)) & 1u)) freemask |= 1u << j;
+        c += stride;
+        if (c >= V) c -= V;
+      }
+      int total;
+      int rank = block_exclusive_scan(__popc(freemask), scratch, &total) + seen;
+#pragma unroll
+      for (int j = 0; j < kWalk; ++j) {
+        if ((freemask >> j) & 1u) {
+          if (rank < need) atomicOr(&aux[cls[j] >> 5], 1u << (cls[j] & 31));
+          ++rank;
+        }
+      }
+      seen += total;
+    }
+    __syncthreads();
+    const int wpt = (W + nt - 1) / nt;  // contiguous words per lane keeps class order
+    const int w0 = min(W, tid * wpt), w1 = min(W, w0 + wpt);
+    if (seen >= need) {
+      for (int w = tid; w < W; w += nt) mark[w] |= aux[w];
+    } else {
+      // 3. Fallback: every step-th free class in ascending order, first `need`.
+      const int step = max(1, (V - distinct) / need);
+      int nfree = 0;
+      for (int w = w0; w < w1; ++w) nfree += __popc(~mark[w] & valid_bits(w, V));
+      int total;
+      int r = block_exclusive_scan(nfree, scratch, &total);
+      for (int w = w0; w < w1; ++w) {
+        uint32_t fm = ~mark[w] & valid_bits(w, V);
+        uint32_t sel = 0;
+        while (fm) {
+          const int b = __ffs(fm) - 1;
+          fm &= fm - 1;
+          if (r % step == 0 && r / step < need) sel |= 1u << b;
+          ++r;
+        }
+        mark[w] |= sel;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4. Ascending compaction: per-word prefix counts, then class -> position.
+  {
+    const int wpt = (W + nt - 1) / nt;
+    const int w0 = min(W, tid * wpt), w1 = min(W, w0 + wpt);
+    int pc = 0;
+    for (int w = w0; w < w1; ++w) pc += __popc(mark[w]);
+    int total;
+    int r = block_exclusive_scan(pc, scratch, &total);
+    for (int w = w0; w < w1; ++w) {
+      aux[w] = (uint32_t)r;
+      r += __popc(mark[w]);
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < V; c += nt) {
+    const uint32_t m = mark[c >> 5];
+    const int b = c & 31;
+    if ((m >> b) & 1u) {
+      const int pos = (int)aux[c >> 5] + __popc(m & ((1u << b) - 1u));
+      vocab_pos[c] = pos;
+      C[pos] = c;
+    } else {
+      vocab_pos[c] = -1;
+    }
+  }
+  if (tid == 0) {
+    counters[kDistinct] = distinct;
+    counters[kNextOffset] = next_off;
+  }
+}
+
+// Labels -> positions in C (identity when P == 0); counts N.
+__global__ __launch_bounds__(256) void k_cand_remap(const int64_t* __restrict__ targets,
+                                                    const int64_t* __restrict__ prefix, int T,
+                                                    int V, int P,
+                                                    const int32_t* __restrict__ vocab_pos,
+                                                    int32_t* __restrict__ target_pos,
+                                                    int32_t* __restrict__ prefix_pos,
+                                                    int32_t* __restrict__ counters) {
+  __shared__ int scratch[256 / kWave + 1];
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  int n = 0;
+  if (t < T) {
+    const int64_t y = targets[t];
+    int tp = -1;
+    if (y >= 0 && y < V) tp = P == 0 ? (int)y : vocab_pos[y];
+    target_pos[t] = tp;
+    n += tp >= 0;
+    int pp = -1;
+    if (prefix != nullptr) {
+      const int64_t p = prefix[t];
+      if (p >= 0 && p < V) pp = P == 0 ? (int)p : vocab_pos[p];
+    }
+    prefix_pos[t] = pp;
+    n += pp >= 0;
+  }
+  const int s = block_sum_int(n, scratch);
+  if (threadIdx.x == 0 && s) atomicAdd(&counters[kNumLabels], s);
+}
+
+__global__ void k_write_aux(const int32_t* __restrict__ counters, int64_t* __restrict__ aux) {
+  if (threadIdx.x == 0) {
+    aux[0] = counters[kDistinct];
+    aux[1] = counters[kNumLabels];
+    aux[2] = counters[kNextOffset];
+    aux[3] = counters[kStatus];
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
+                             int stride, int off, uint8_t* bytemap, int32_t* counters,
+                             int32_t* C, int32_t* vocab_pos, int32_t* target_pos,
+                             int32_t* prefix_pos, hipStream_t s) {
+  const int nvec = bytemap_bytes(V) / 16;
+  const int init_threads = nvec > kNumCounters ? nvec : kNumCounters;
+  hipLaunchKernelGGL(k_cand_init, dim3((init_threads + 255) / 256), dim3(256), 0, s,
+                     reinterpret_cast<uint4*>(bytemap), nvec, counters);
+  if (T > 0)
+    hipLaunchKernelGGL(k_cand_mark, dim3((T + 255) / 256), dim3(256), 0, s, targets, prefix, T,
+                       V, bytemap, counters);
+  const size_t lds = P > 0 ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
+  hipLaunchKernelGGL(k_cand_build, dim3(1), dim3(kBuildThreads), lds, s, bytemap, V, P, stride,
+                     off, C, vocab_pos, counters);
+  if (T > 0)
+    hipLaunchKernelGGL(k_cand_remap, dim3((T + 255) / 256), dim3(256), 0, s, targets, prefix, T,
+                       V, P, vocab_pos, target_pos, prefix_pos, counters);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s) {
+  hipLaunchKernelGGL(k_write_aux, dim3(1), dim3(64), 0, s, counters, aux);
+  return hipGetLastError();
+}
+
+}  // namespace sce

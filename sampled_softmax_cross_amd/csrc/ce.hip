@@ -1,0 +1,331 @@
+// Fused row-wise cross-entropy forward + backward over the logits, in place.
+//
+// Per row t of Z [T, ldz] (P valid columns; columns [P, ldz) are padding):
+//   L_t   = m_t + ln sum_j exp(Z_tj - m_t),  m_t = max_j Z_tj
+//   loss_t = [y'>=0](L_t - Z_ty') + [p'>=0](L_t - Z_tp')
+//   dZ_tj = (n_t exp(Z_tj - L_t) - [j=y'] - [j=p']) / N     (written over Z)
+// ("Learning Triton one kernel at a time: softmax": max subtraction, the online
+// softmax that merges running (max, sum) pairs, and the softmax gradient, here
+// specialised to cross-entropy where the upstream gradient is a one-hot.)
+//
+// The row is read from HBM once into registers and written once: the kernel
+// never re-reads Z and allocates no second [T, P] buffer. Each lane keeps its
+// slice of the row as exp(Z - m_lane) after the first sweep, so the gradient
+// costs one multiply per element; lanes merge their (max, sum) pairs with the
+// online-softmax rule (rescale the smaller-max sum by exp(m_small - m_big)).
+#include "common.h"
+#include "kernels.h"
+
+namespace sce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename TZ>
+struct RowVec;  // 16 bytes of a row
+
+template <>
+struct RowVec<bf16_t> {
+  static constexpr int kElems = 8;
+  __device__ static void unpack(const uint4& q, float* f) {
+    f[0] = bf16_lo(q.x); f[1] = bf16_hi(q.x); f[2] = bf16_lo(q.y); f[3] = bf16_hi(q.y);
+    f[4] = bf16_lo(q.z); f[5] = bf16_hi(q.z); f[6] = bf16_lo(q.w); f[7] = bf16_hi(q.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
+  }
+  __device__ static float load1(const bf16_t* p) { return bf16_to_f32(*p); }
+};
+
+template <>
+struct RowVec<float> {
+  static constexpr int kElems = 4;
+  __device__ static void unpack(const uint4& q, float* f) {
+    f[0] = __uint_as_float(q.x); f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z); f[3] = __uint_as_float(q.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+  __device__ static float load1(const float* p) { return *p; }
+};
+
+// Merge two (max, sum) pairs of the online softmax; a max of -inf marks an empty pair.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * __builtin_amdgcn_exp2f((m - M) * kLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - M) * kLog2e);
+  m = M;
+}
+
+// Block-wide merge; every thread gets the row's (max, sum). Contains barriers.
+template <int NT>
+__device__ __forceinline__ void block_merge_ms(float& m, float& s, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave);
+    const float s2 = __shfl_xor(s, o, kWave);
+    merge_ms(m, s, m2, s2);
+  }
+  constexpr int NW = NT / kWave;
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[2 * wid] = m;
+    red[2 * wid + 1] = s;
+  }
+  __syncthreads();
+  float M = red[0], S = red[1];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) merge_ms(M, S, red[2 * w], red[2 * w + 1]);
+  m = M;
+  s = S;
+}
+
+// Register-resident row: NT lanes x VPT vectors of 16 bytes cover the row.
+template <typename TZ, int NT, int VPT>
+__global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz, int P,
+                                                const int32_t* __restrict__ tpos,
+                                                const int32_t* __restrict__ ppos,
+                                                const int32_t* __restrict__ counters,
+                                                float* __restrict__ row_loss,
+                                                float* __restrict__ row_lse) {
+  using RV = RowVec<TZ>;
+  constexpr int E = RV::kElems;
+  __shared__ float red[2 * (NT / kWave)];
+  __shared__ float zlab[2];
+  const int t = blockIdx.x;
+  TZ* row = Z + (int64_t)t * ldz;
+  uint4* rowv = reinterpret_cast<uint4*>(row);
+  const int nvec = (int)(ldz / E);  // vectors in the padded row
+  const int tp = tpos[t];
+  const int pp = ppos[t];
+  if (threadIdx.x == 0) {
+    zlab[0] = tp >= 0 ? RV::load1(row + tp) : 0.f;
+    zlab[1] = pp >= 0 ? RV::load1(row + pp) : 0.f;
+  }
+
+  float v[VPT][E];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < nvec) {
+      const uint4 q = rowv[i];
+      RV::unpack(q, v[k]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (i * E + e >= P) v[k][e] = -INFINITY;
+        m = fmaxf(m, v[k][e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[k][e] = -INFINITY;
+    }
+  }
+  // exp(Z - m_lane), kept for the gradient; exp2 of -inf is exactly 0.
+  float s = 0.f;
+  const float mb = m == -INFINITY ? 0.f : m * kLog2e;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      v[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][e], kLog2e, -mb));
+      s += v[k][e];
+    }
+  float M = m, S = s;
+  block_merge_ms<NT>(M, S, red);
+  const float L = M + __builtin_amdgcn_logf(S) * kLn2;  // logf here is log2
+
+  const int N = counters[kNumLabels];
+  const float inv = N > 0 ? 1.0f / (float)N : 0.f;
+  const int nt = (tp >= 0) + (pp >= 0);
+  // exp(Z - L) = exp(Z - m_lane) * exp(m_lane - L)
+  const float scale = m == -INFINITY ? 0.f
+                                     : (float)nt * inv * __builtin_amdgcn_exp2f((m - L) * kLog2e);
+  const int vt = tp >= 0 ? tp / E : -1;
+  const int vp = pp >= 0 ? pp / E : -1;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < nvec) {
+      float g[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) g[e] = v[k][e] * scale;  // 0 on padding columns
+      if (i == vt || i == vp) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int j = i * E + e;
+          g[e] -= (float)((j == tp) + (j == pp)) * inv;
+        }
+      }
+      rowv[i] = RV::pack(g);
+    }
+  }
+  if (threadIdx.x == 0) {
+    float l = 0.f;
+    if (tp >= 0) l += L - zlab[0];
+    if (pp >= 0) l += L - zlab[1];
+    row_loss[t] = l;
+    if (row_lse) row_lse[t] = L;
+  }
+}
+
+// Rows too long for registers: two sweeps over HBM (online (max, sum), then write).
+template <typename TZ, int NT>
+__global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64_t ldz, int P,
+                                                       const int32_t* __restrict__ tpos,
+                                                       const int32_t* __restrict__ ppos,
+                                                       const int32_t* __restrict__ counters,
+                                                       float* __restrict__ row_loss,
+                                                       float* __restrict__ row_lse) {
+  using RV = RowVec<TZ>;
+  constexpr int E = RV::kElems;
+  __shared__ float red[2 * (NT / kWave)];
+  __shared__ float zlab[2];
+  const int t = blockIdx.x;
+  TZ* row = Z + (int64_t)t * ldz;
+  uint4* rowv = reinterpret_cast<uint4*>(row);
+  const int nvec = (int)(ldz / E);
+  const int tp = tpos[t];
+  const int pp = ppos[t];
+  if (threadIdx.x == 0) {
+    zlab[0] = tp >= 0 ? RV::load1(row + tp) : 0.f;
+    zlab[1] = pp >= 0 ? RV::load1(row + pp) : 0.f;
+  }
+  float m = -INFINITY, s = 0.f;
+  for (int i = threadIdx.x; i < nvec; i += NT) {
+    float f[E];
+    RV::unpack(rowv[i], f);
+    float cm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (i * E + e >= P) f[e] = -INFINITY;
+      cm = fmaxf(cm, f[e]);
+    }
+    if (cm == -INFINITY) continue;
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cs += __builtin_amdgcn_exp2f((f[e] - cm) * kLog2e);
+    merge_ms(m, s, cm, cs);
+  }
+  block_merge_ms<NT>(m, s, red);
+  const float L = m + __builtin_amdgcn_logf(s) * kLn2;
+  const int N = counters[kNumLabels];
+  const float inv = N > 0 ? 1.0f / (float)N : 0.f;
+  const float c = (float)((tp >= 0) + (pp >= 0)) * inv;
+  __syncthreads();  // zlab was read before any lane writes the row
+  for (int i = threadIdx.x; i < nvec; i += NT) {
+    float f[E];
+    RV::unpack(rowv[i], f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = i * E + e;
+      f[e] = j < P ? c * __builtin_amdgcn_exp2f((f[e] - L) * kLog2e) -
+                         (float)((j == tp) + (j == pp)) * inv
+                   : 0.f;
+    }
+    rowv[i] = RV::pack(f);
+  }
+  if (threadIdx.x == 0) {
+    float l = 0.f;
+    if (tp >= 0) l += L - zlab[0];
+    if (pp >= 0) l += L - zlab[1];
+    row_loss[t] = l;
+    if (row_lse) row_lse[t] = L;
+  }
+}
+
+template <typename TZ, int NT, int VPT>
+static void launch_ce_fixed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp, const int32_t* pp,
+                            const int32_t* counters, float* rl, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL((k_ce_rows<TZ, NT, VPT>), dim3(T), dim3(NT), 0, s, Z, ldz, P, tp, pp, counters,
+                     rl, lse);
+}
+
+template <typename TZ, int NT>
+static bool launch_ce_nt(int vpt, TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
+                         const int32_t* pp, const int32_t* counters, float* rl, float* lse,
+                         hipStream_t s) {
+  switch (vpt) {
+#define SCE_CE_CASE(n) \
+  case n:              \
+    launch_ce_fixed<TZ, NT, n>(Z, ldz, T, P, tp, pp, counters, rl, lse, s); \
+    return true;
+    SCE_CE_CASE(1) SCE_CE_CASE(2) SCE_CE_CASE(3) SCE_CE_CASE(4) SCE_CE_CASE(5) SCE_CE_CASE(6)
+    SCE_CE_CASE(7) SCE_CE_CASE(8) SCE_CE_CASE(9) SCE_CE_CASE(10) SCE_CE_CASE(11) SCE_CE_CASE(12)
+    SCE_CE_CASE(13) SCE_CE_CASE(14) SCE_CE_CASE(15) SCE_CE_CASE(16)
+#undef SCE_CE_CASE
+    default:
+      return false;
+  }
+}
+
+template <typename TZ>
+static void launch_ce_typed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
+                            const int32_t* pp, const int32_t* counters, float* rl, float* lse,
+                            hipStream_t s) {
+  constexpr int E = RowVec<TZ>::kElems;
+  const int64_t nvec = ldz / E;
+  if (nvec <= 256 * 16) {
+    launch_ce_nt<TZ, 256>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse, s);
+  } else if (nvec <= 512 * 16) {
+    launch_ce_nt<TZ, 512>((int)((nvec + 511) / 512), Z, ldz, T, P, tp, pp, counters, rl, lse, s);
+  } else {
+    hipLaunchKernelGGL((k_ce_rows_stream<TZ, 1024>), dim3(T), dim3(1024), 0, s, Z, ldz, P, tp, pp,
+                       counters, rl, lse);
+  }
+}
+
+hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
+                          const int32_t* target_pos, const int32_t* prefix_pos,
+                          const int32_t* counters, float* row_loss, float* row_lse,
+                          hipStream_t s) {
+  if (T <= 0) return hipGetLastError();
+  if (bf16)
+    launch_ce_typed<bf16_t>(static_cast<bf16_t*>(Z), ldz, T, P, target_pos, prefix_pos, counters,
+                            row_loss, row_lse, s);
+  else
+    launch_ce_typed<float>(static_cast<float*>(Z), ldz, T, P, target_pos, prefix_pos, counters,
+                           row_loss, row_lse, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// loss = sum_t row_loss[t] / N, summed in a fixed order (deterministic).
+constexpr int kFinalizeThreads = 1024;
+
+__global__ __launch_bounds__(kFinalizeThreads) void k_finalize(const float* __restrict__ row_loss,
+                                                               int T,
+                                                               const int32_t* __restrict__ counters,
+                                                               float* __restrict__ loss,
+                                                               int64_t* __restrict__ aux) {
+  __shared__ double red[kFinalizeThreads / kWave];
+  double acc = 0.0;
+  for (int t = threadIdx.x; t < T; t += kFinalizeThreads) acc += (double)row_loss[t];
+  acc = wave_sum(acc);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int w = 0; w < kFinalizeThreads / kWave; ++w) tot += red[w];
+    const int N = counters[kNumLabels];
+    *loss = N > 0 ? (float)(tot / (double)N) : 0.f;
+    if (aux) {
+      aux[0] = counters[kDistinct];
+      aux[1] = N;
+      aux[2] = counters[kNextOffset];
+      aux[3] = counters[kStatus];
+    }
+  }
+}
+
+hipError_t launch_finalize(const float* row_loss, int T, const int32_t* counters, float* loss,
+                           int64_t* aux, hipStream_t s) {
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeThreads), 0, s, row_loss, T, counters, loss,
+                     aux);
+  return hipGetLastError();
+}
+
+}  // namespace sce

@@ -1,0 +1,34 @@
+"""Helpers for the GPU parity tests: device transfer and error measures."""
+import numpy as np
+import torch
+
+from sampled_softmax_cross_amd import synth
+
+
+def to_dev(a, dtype):
+    """numpy input (bf16 bits as uint16, or float32) -> device tensor of that dtype."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def labels_dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).cuda()
+
+
+def to_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def max_rel(got, ref):
+    """max |got - ref| / max |ref| over the tensor (the tolerance measure for dX, dW)."""
+    den = np.abs(ref).max()
+    num = np.abs(got - ref).max()
+    return num / den if den > 0 else num
+
+
+TOL = {"bf16": dict(loss=1e-3, grad=2e-2), "f32": dict(loss=1e-5, grad=1e-5)}
+
+
+def inputs_f64(x, W, dtype):
+    return synth.to_f64(x, dtype), synth.to_f64(W, dtype)

@@ -1,0 +1,84 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the header
+declares, and its host-side argument checks behave (no GPU work is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sampled_softmax_cross_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "sampled_ce.h")).read()
+    return sorted(set(re.findall(r"^SCE_API\s+(?:sce_status|const char\*|int)\s+(\w+)\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sampled_softmax_cross_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sce_abi_version() == 1
+    for code in range(4):
+        assert lib.sce_status_string(code).decode().startswith("SCE_")
+    assert lib.sce_status_string(99) == b"unknown sce_status"
+
+
+def _ws(T, d, V, P, dt):
+    out = ctypes.c_size_t(0)
+    rc = binding.load_library().sce_workspace_size(T, d, V, P, dt, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_size_host_checks(lib):
+    rc, n = _ws(16384, 768, 50304, 10240, binding.SCE_BF16)
+    assert rc == 0
+    # the [T, P] logits buffer dominates
+    assert n >= 16384 * 10240 * 2
+    rc0, n0 = _ws(49152, 768, 50304, 0, binding.SCE_BF16)
+    assert rc0 == 0 and n0 >= 49152 * 50304 * 2
+    assert _ws(10, 7, 100, 10, binding.SCE_BF16)[0] == 1      # d not a multiple of 8
+    assert _ws(10, 8, 100, 101, binding.SCE_BF16)[0] == 1     # P > V
+    assert _ws(10, 8, 100, -1, binding.SCE_BF16)[0] == 1      # P < 0
+    assert _ws(10, 8, 100, 10, 7)[0] == 1                     # bad dtype
+    assert _ws(-1, 8, 100, 10, 0)[0] == 1                     # T < 0
+    assert _ws(10, 8, 131073, 10, 0)[0] == 1                 # V too large for a candidate build
+    assert _ws(10, 8, 1 << 20, 0, 0)[0] == 0                  # ... fine for the full softmax
+    assert lib.sce_workspace_size(1, 8, 8, 1, 0, None) == 1   # null output pointer
+
+
+def test_forward_backward_host_checks(lib):
+    f = lib.sampled_ce_forward_backward
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    args = dict(x=fake, W=fake, y=fake, p=None, T=4, d=8, V=16, P=4, stride=3, off=0, dt=0,
+                loss=fake, dX=fake, dW=fake, c=None, tp=None, pp=None, lse=None, rl=None,
+                aux=None, ws=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    assert call() == 2                                  # no workspace
+    assert call(stride=4) == 1                          # gcd(4, 16) != 1
+    assert call(P=17) == 1                              # P > V
+    assert call(d=12) == 1                              # d % 8 != 0
+    assert call(W=None) == 1
+    assert call(x=ctypes.c_void_p((1 << 20) + 2)) == 1  # misaligned
+    assert call(ws=fake, wsb=16) == 2                   # too small
+    b = lib.sce_build_candidates
+    assert b(fake, None, 4, 16, 0, 3, 0, fake, None, fake, None, None, fake, 1 << 30, None) == 1  # P = 0
+    assert b(fake, None, 4, 16, 4, 2, 0, fake, None, fake, None, None, fake, 1 << 30, None) == 1  # gcd

@@ -1,0 +1,131 @@
+"""Whole step (sampled_ce_forward_backward) vs the dense oracle on small shapes that
+span several GEMM tiles and CE vectors, with ragged tails in every dimension, plus
+the bitwise invariants of the ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import build_candidates, ce
+from sampled_softmax_cross_amd import binding, synth
+from tests.gpu_util import TOL, inputs_f64, labels_dev, max_rel, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # T, d, V, P, dtype, prefix, ignore_frac, stride
+    (512, 128, 4096, 2048, "f32", False, 0.0, 1021),   # the tiny workload's shape
+    (512, 128, 4096, 2048, "bf16", True, 0.1, 1021),
+    (300, 64, 1000, 333, "bf16", True, 0.05, 7),        # ragged T, P; P % 8 != 0
+    (300, 64, 1000, 333, "f32", True, 0.05, 7),
+    (257, 136, 777, 0, "bf16", True, 0.0, 1),           # full softmax, ragged V and d
+    (257, 136, 777, 0, "f32", False, 0.2, 1),
+    (1000, 256, 3000, 1500, "bf16", True, 0.0, 7),
+    (129, 8, 50, 50, "f32", True, 0.3, 3),              # d = 8, P = V
+    (64, 768, 50304, 10240, "bf16", True, 0.0, 20011),  # full vocabulary and hidden size
+    (2050, 96, 2500, 1601, "bf16", False, 0.0, 3),
+]
+
+
+def _step(x, W, y, p, P, stride, offset, dtype, rows=True):
+    out = binding.forward_backward(to_dev(x, dtype), to_dev(W, dtype), labels_dev(y), labels_dev(p),
+                                   P, stride, offset, want_rows=rows)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("T,d,V,P,dtype,prefix,ign,stride", CASES)
+def test_step_matches_oracle(T, d, V, P, dtype, prefix, ign, stride):
+    print(f"step T={T} d={d} V={V} P={P} {dtype}", flush=True)
+    x, W, y, p = synth.small_case(T + V + P, T, d, V, dtype, prefix=prefix, ignore_frac=ign)
+    offset = (T * 7) % V
+    out = _step(x, W, y, p, P, stride, offset, dtype)
+    cand = build_candidates(V, P, stride, offset, y, p)
+    xf, Wf = inputs_f64(x, W, dtype)
+    C = None if P == 0 else cand["C"]
+    ppos = cand["prefix_pos"] if p is not None else None
+    loss, dX, dW, L, row_loss = ce.forward_backward(xf, Wf, C, cand["target_pos"], ppos)
+    tol = TOL[dtype]
+    # integers: exact
+    if P > 0:
+        assert np.array_equal(out["C"].cpu().numpy(), cand["C"])
+    assert np.array_equal(out["target_pos"].cpu().numpy(), cand["target_pos"])
+    assert np.array_equal(out["prefix_pos"].cpu().numpy(), cand["prefix_pos"])
+    aux = out["aux"].cpu().numpy()
+    assert aux.tolist() == [cand["num_targets"], cand["N"], cand["next_offset"] if P else offset, 0]
+    # floating point: the stated tolerances
+    got = float(out["loss"].item())
+    assert abs(got - loss) <= tol["loss"] * abs(loss), (got, loss)
+    np.testing.assert_allclose(to_f64(out["row_lse"]), L, rtol=tol["loss"], atol=0)
+    assert max_rel(to_f64(out["row_loss"]), row_loss) <= tol["loss"] * 10
+    gX, gW = to_f64(out["dX"]), to_f64(out["dW"])
+    assert max_rel(gX, dX) <= tol["grad"], max_rel(gX, dX)
+    assert max_rel(gW, dW) <= tol["grad"], max_rel(gW, dW)
+    if P > 0:
+        outside = np.setdiff1d(np.arange(V), cand["C"])
+        raw = out["dW"].cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy()
+        assert (raw[outside] == 0).all()  # exactly +0.0
+
+
+def test_p0_equals_pv_bitwise():
+    T, d, V = 300, 64, 1000
+    for dtype in ("bf16", "f32"):
+        x, W, y, p = synth.small_case(3, T, d, V, dtype, prefix=True, ignore_frac=0.1)
+        a = _step(x, W, y, p, 0, 7, 0, dtype)
+        b = _step(x, W, y, p, V, 7, 0, dtype)
+        for k in ("loss", "dX", "dW", "row_lse", "row_loss", "target_pos", "prefix_pos"):
+            assert torch.equal(a[k], b[k]), k
+
+
+def test_noop_prefix_bitwise_and_determinism():
+    T, d, V, P = 300, 64, 1000, 400
+    x, W, y, _ = synth.small_case(4, T, d, V, "bf16", prefix=False)
+    none = _step(x, W, y, None, P, 7, 9, "bf16")
+    noop = _step(x, W, y, np.full(T, -1, dtype=np.int64), P, 7, 9, "bf16")
+    again = _step(x, W, y, None, P, 7, 9, "bf16")
+    for k in ("loss", "dX", "dW", "row_lse", "row_loss", "C", "target_pos"):
+        assert torch.equal(none[k], noop[k]), k
+        assert torch.equal(none[k], again[k]), k
+
+
+def test_no_labels_and_empty_batch():
+    T, d, V, P = 100, 64, 500, 200
+    x, W, y, p = synth.small_case(5, T, d, V, "bf16", prefix=True)
+    y[:] = -1
+    p[:] = -1
+    out = _step(x, W, y, p, P, 7, 0, "bf16")
+    assert out["loss"].item() == 0.0
+    assert not out["dX"].float().abs().sum().item() and not out["dW"].float().abs().sum().item()
+    assert out["aux"].cpu().tolist()[1] == 0
+    # T = 0: the candidate set is the first P window classes; loss 0, dW 0
+    dev = torch.device("cuda")
+    xt = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    Wt = to_dev(W, "bf16")
+    o = binding.forward_backward(xt, Wt, torch.empty(0, dtype=torch.int64, device=dev), None, P, 7, 0)
+    torch.cuda.synchronize()
+    cand = build_candidates(V, P, 7, 0, np.zeros(0, dtype=np.int64))
+    assert np.array_equal(o["C"].cpu().numpy(), cand["C"])
+    assert o["loss"].item() == 0.0 and not o["dW"].float().abs().sum().item()
+
+
+def test_closed_form_zero_hidden():
+    """x = 0: every logit is 0, so the loss is ln P exactly (up to fp32) and dW = 0."""
+    T, d, V, P = 256, 64, 2000, 1024
+    _, W, y, p = synth.small_case(6, T, d, V, "bf16", prefix=True)
+    x = np.zeros((T, d), dtype=np.uint16)
+    out = _step(x, W, y, p, P, 7, 0, "bf16")
+    assert math.isclose(out["loss"].item(), math.log(P), rel_tol=1e-6)
+    assert not out["dW"].float().abs().sum().item()
+
+
+def test_label_out_of_range_is_flagged_not_faulted():
+    T, d, V, P = 64, 64, 500, 100
+    x, W, y, p = synth.small_case(7, T, d, V, "bf16", prefix=True)
+    y[3] = V + 5
+    p[4] = -7
+    out = _step(x, W, y, p, P, 7, 0, "bf16")
+    assert out["aux"].cpu().numpy()[3] & binding.DEV_LABEL_RANGE
+    y = np.arange(T, dtype=np.int64)  # 64 distinct targets > P = 50
+    out = _step(x, W, y, None, 50, 7, 0, "bf16")
+    assert out["aux"].cpu().numpy()[3] & binding.DEV_TOO_MANY_TARGETS
