@@ -29,8 +29,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_work(w, P_eff, splits):
-    """Algorithmic work of one launch of each stage: (kind, amount, unit)."""
+def stage_work(w, P_eff):
+    """Algorithmic work of one launch of each stage: (kind, amount)."""
     es = 2 if w.dtype == "bf16" else 4
     ldz = (P_eff + 7) // 8 * 8
     flops = 2.0 * w.T * P_eff * w.d
@@ -41,16 +41,16 @@ def stage_work(w, P_eff, splits):
         # read Z once, write dZ once, plus labels and the row loss
         "ce": ("hbm", 2.0 * w.T * ldz * es + w.T * 12),
         "gather": ("hbm", 2.0 * w.P * w.d * es + 4 * w.P),
-        # read the fp32 split-K partials of the candidate rows, write dense dW, read vocab_pos
-        "scatter": ("hbm", splits * P_eff * w.d * 4.0 + w.V * w.d * es + 4 * w.V),
+        # read the fp32 candidate-row gradient once, write the dense dW, read vocab_pos
+        "scatter": ("hbm", P_eff * w.d * 4.0 + w.V * w.d * es + 4 * w.V),
     }
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="stage01")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
@@ -119,8 +119,7 @@ def main():
     stage_ms, ncalls = binding.profile_collect()
     stage_ms = {k: v / ncalls for k, v in stage_ms.items()}
     P_eff = w.P if w.P else w.V
-    splits = binding.load_library() and _dw_splits(P_eff, w.d, w.T)
-    work = stage_work(w, P_eff, splits)
+    work = stage_work(w, P_eff)
     stages = {}
     for k, t in stage_ms.items():
         entry = {"ms": round(t, 5)}
@@ -181,15 +180,6 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
-
-
-def _dw_splits(M, N, K):
-    """Split-K factor the library uses for the dW GEMM (mirrors gemm_dw_splits)."""
-    tiles = ((M + 127) // 128) * ((N + 127) // 128)
-    s = 1
-    while s < 16 and tiles * s < 512 and K // (2 * s) >= 1024:
-        s *= 2
-    return s
 
 
 def cpu_baseline(w, x, W, y, p, sample_tokens):

@@ -60,6 +60,7 @@ typedef enum sce_dtype { SCE_F32 = 0, SCE_BF16 = 1 } sce_dtype;
 
 /* Limits checked on the host. */
 #define SCE_MAX_V_SAMPLED 131072 /* V limit when P > 0 (two candidate bitmaps held in LDS) */
+#define SCE_MAX_V 1048576        /* V limit for the full softmax (32-bit tile offsets) */
 #define SCE_MAX_D 16384
 
 /*

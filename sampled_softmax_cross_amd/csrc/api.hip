@@ -31,7 +31,8 @@ int64_t mod64(int64_t a, int64_t m) {
 // Byte offsets of every workspace piece.
 struct Plan {
   int64_t Peff = 0, ldz = 0;
-  int splits = 1;
+  int splits = 1;     // k-split of the dW product (fp32 partials reduced by the scatter)
+  int dx_splits = 1;  // k-split of the dX product (fp32 partials reduced into dX)
   size_t counters = 0, bytemap = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
   size_t wc = 0, z = 0, part = 0, total = 0;
 };
@@ -58,8 +59,16 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
   if (full) {
     p.wc = take(P > 0 ? (size_t)P * d * es : 0);
     p.z = take((size_t)T * p.ldz * es);
-    p.splits = gemm_dw_splits(p.Peff, d, T);
-    p.part = take((size_t)p.splits * p.Peff * d * sizeof(float));
+    if (dtype == SCE_BF16) {
+      p.splits = gemm_bf16_splits(p.Peff, d, T, 8);
+      p.dx_splits = gemm_bf16_splits(T, d, p.Peff, 4);
+    } else {
+      p.splits = gemm_dw_splits(p.Peff, d, T);
+    }
+    // One region serves both products' partials (dX's are reduced before dW runs).
+    const size_t dw_part = (size_t)p.splits * p.Peff * d;
+    const size_t dx_part = p.dx_splits > 1 ? (size_t)p.dx_splits * T * d : 0;
+    p.part = take((dw_part > dx_part ? dw_part : dx_part) * sizeof(float));
   }
   p.total = off;
   return p;
@@ -69,7 +78,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 sce_status check_sizes(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool need_d) {
   if (T < 0 || T > INT32_MAX / 2) return SCE_EINVAL;
-  if (V < 1 || V > INT32_MAX / 2) return SCE_EINVAL;
+  if (V < 1 || V > SCE_MAX_V) return SCE_EINVAL;
   if (P < 0 || P > V) return SCE_EINVAL;
   if (P > 0 && V > SCE_MAX_V_SAMPLED) return SCE_EINVAL;
   if (need_d && (d < 8 || d % 8 != 0 || d > SCE_MAX_D)) return SCE_EINVAL;
@@ -217,8 +226,15 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   if (e == hipSuccess) e = launch_finalize(row_loss, (int)T, counters, loss, aux_out, hs);
   marks.mark(SCE_STAGE_DX);
   if (e == hipSuccess && T > 0) {
-    GemmArgs g{Z, p.ldz, WC, d, dX, d, T, d, p.Peff, 1, 0};
-    e = launch_gemm(Gemm::DX, bf16, g, hs);
+    if (p.dx_splits > 1) {
+      GemmArgs g{Z, p.ldz, WC, d, part, d, T, d, p.Peff, p.dx_splits, T * d};
+      e = launch_gemm(Gemm::DX, bf16, g, hs);
+      if (e == hipSuccess)
+        e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, bf16, dX, hs);
+    } else {
+      GemmArgs g{Z, p.ldz, WC, d, dX, d, T, d, p.Peff, 1, 0};
+      e = launch_gemm(Gemm::DX, bf16, g, hs);
+    }
   }
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess) {

@@ -1,0 +1,329 @@
+// Multi-stage bf16 MFMA GEMM for gfx950 (the logits, dX and dW products of the step).
+//
+// Every operand tile travels global -> LDS by buffer_load ... lds (no VGPR staging,
+// no ds_write), through an NS-deep ring of LDS stages of 32 k each, so a tile is
+// requested NS-1 stage-times before the MFMAs need it and the load latency of a
+// busy memory system stays hidden behind the matrix cores.
+//
+// Operand layouts in LDS:
+//  * r-major (element (r, k) at P[r * ld + k], k contiguous): rows of 32 k = 64 B,
+//    the four 16-byte chunks of a row XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3;
+//    a fragment (8 consecutive k of one row) is one ds_read_b128.
+//  * k-major (element (r, k) at P[k * ld + r]): the tile is kept as it is in memory,
+//    32 rows of k, each R elements wide, 16-byte chunks XOR-swizzled by 4 * (k & 3).
+//    Fragments are read with ds_read_b64_tr_b16: within each 16-lane group, lane j
+//    receives element i from the address supplied by lane 4i + j/4 (at element
+//    offset j % 4), so lanes that point at rows k..k+3 and 4-column groups assemble
+//    8-k fragments of single columns without any transpose pass.
+// Both swizzles spread a fragment read over all LDS banks; the DMA fill picks, for
+// each lane, the global chunk that belongs at its (linear) LDS position.
+//
+// The MFMA (v_mfma_f32_32x32x16_bf16) takes the B-tile fragment first, which makes
+// every accumulator block the transposed output and lets the epilogue write 16-byte
+// vectors straight from registers (see store_acc).
+#include "gemm_common.h"
+
+namespace sce {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+constexpr int kStageK = 32;  // k per LDS stage
+
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt at their maxima (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// vmcnt(LPS * min(after, I)), chosen at run time among compile-time immediates.
+template <int LPS, int I>
+__device__ __forceinline__ void wait_after(int after) {
+  if constexpr (I <= 0) {
+    vm_wait<0>();
+  } else {
+    if (after >= I) vm_wait<LPS * I>();
+    else wait_after<LPS, I - 1>(after);
+  }
+}
+
+__device__ __forceinline__ int rm_index(int row, int ch) {
+  return row * 4 + (ch ^ (((row >> 1) ^ (row >> 3)) & 3));
+}
+template <int R>
+__device__ __forceinline__ int km_index(int k, int ch) {
+  return k * (R / 8) + (ch ^ ((k & 3) << 2));
+}
+
+// One operand tile of R rows (r-major) or R columns (k-major) per stage.
+template <int R, bool KMAJ>
+struct DmaTile {
+  static_assert(R % 64 == 0 && (!KMAJ || R % 128 == 0), "tile shape");
+  static constexpr int kN = R / 64;  // DMA instructions per wave per stage
+  int off[kN];  // byte offset of the lane's chunk from the tile origin
+  int kk[kN];   // k of the lane's chunk (r-major) or row (k-major), for the k clip
+  int rr[kN];   // row (r-major) or first column (k-major) of the lane's chunk
+  __device__ __forceinline__ void init(int64_t ld) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int q = 64 * (w * kN + i) + lane;  // linear LDS chunk this lane fills
+      int r, k;
+      if constexpr (!KMAJ) {
+        r = q >> 2;
+        k = ((q & 3) ^ (((r >> 1) ^ (r >> 3)) & 3)) * 8;
+      } else {
+        k = q / (R / 8);
+        r = ((q % (R / 8)) ^ ((k & 3) << 2)) * 8;
+      }
+      kk[i] = k;
+      rr[i] = r;
+      off[i] = (int)((KMAJ ? (int64_t)k * ld + r : (int64_t)r * ld + k) * 2);
+    }
+  }
+  // base: address of tile element (0, 0) of this stage; rows_valid / k_valid clip the
+  // tile (a clipped chunk reads zeros).
+  __device__ __forceinline__ void issue(const bf16_t* base, int64_t rows_valid, int64_t k_valid,
+                                        uint4* tile) const {
+    const rsrc_t rs = make_rsrc(base);
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(tile + (w * kN + i) * 64), 16,
+          (kk[i] < k_valid && rr[i] < rows_valid) ? off[i] : kOOB, 0, 0, 0);
+  }
+};
+
+// Fragment of 8 consecutive k (k-step ks of the stage) for tile row/column `r`
+// (this lane's own; r already includes lane % 32).
+template <int R, bool KMAJ>
+__device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int r_blk, int ks,
+                                              int lane) {
+  if constexpr (!KMAJ) {
+    return __builtin_bit_cast(bf16x8_t, tile[rm_index(r_lane, 2 * ks + (lane >> 5))]);
+  } else {
+    const int G = lane >> 4, a = lane & 15;
+    const int c = r_blk + 16 * (G & 1) + 4 * (a & 3);  // column this lane points at
+    const char* base = reinterpret_cast<const char*>(tile);
+    i16x4_t h[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int k = 16 * ks + 8 * (G >> 1) + 4 * h2 + (a >> 2);
+      const int byte = km_index<R>(k, c >> 3) * 16 + (c & 7) * 2;
+      h[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(base + byte));
+    }
+    typedef short i16x8_t __attribute__((ext_vector_type(8)));
+    const i16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// Persistent kernel: each workgroup takes the work units (output tile, k-split)
+// u = blockIdx.x, blockIdx.x + gridDim.x, ... and streams their k-stages through one
+// NS-deep LDS ring without a break between units: the first stages of the next unit
+// are already in flight while the current unit finishes and stores its tile.
+// BM x BN tile per unit, 4 waves as WGM x (4 / WGM); OCC workgroups share a CU.
+template <int BM, int BN, int WGM, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
+__global__ __launch_bounds__(kGemmThreads, OCC) void k_gemm_bf16(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
+    void* __restrict__ Cout, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t kps,
+    int64_t split_stride, int splits) {
+  constexpr int WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = (BM + BN) * 4;  // uint4 per stage (64 B per row/column)
+  constexpr int LPS = BM / 64 + BN / 64;  // DMA instructions per wave per stage
+  static_assert(NS >= 3 && LPS * (NS - 1) < 64, "pipeline depth");
+  __shared__ uint4 lds[NS * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int wm = wid / WGN, wn = wid % WGN;
+  const int nbx = (int)((N + BN - 1) / BN), nby = (int)((M + BM - 1) / BM);
+  const int ntiles = nbx * nby;
+  const int nunits = ntiles * splits;
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= nunits) return;
+  const int my_units = (nunits - 1 - (int)blockIdx.x) / G + 1;
+  const int nk = (int)(kps / kStageK);  // stages per unit (kps is a positive multiple)
+
+  struct Unit {
+    int64_t m0, n0, kb, ke;
+  };
+  auto unit = [&](int i) {
+    const int u = (int)blockIdx.x + i * G;
+    const int t = u % ntiles;
+    int tm, tn;
+    tile_of(t, nby, nbx, tm, tn);
+    Unit c;
+    c.m0 = (int64_t)tm * BM;
+    c.n0 = (int64_t)tn * BN;
+    c.kb = (int64_t)(u / ntiles) * kps;
+    c.ke = K < c.kb + kps ? K : c.kb + kps;
+    return c;
+  };
+
+  DmaTile<BM, A_KM> ta;
+  DmaTile<BN, B_KM> tb;
+  ta.init(lda);
+  tb.init(ldb);
+  // Issue cursor: unit iu, stage is of that unit. Past the last unit, stages are
+  // issued fully clipped (zeros, no memory traffic) so every wait count is constant.
+  int iu = 0, is = 0;
+  Unit ic = unit(0);
+  auto issue_next = [&](int slot_idx) {
+    uint4* slot = lds + slot_idx * STAGE;
+    const int64_t k0 = ic.kb + (int64_t)is * kStageK;
+    const bool live = iu < my_units;
+    const int64_t kv = live ? ic.ke - k0 : 0;
+    ta.issue(A_KM ? A + k0 * lda + ic.m0 : A + ic.m0 * lda + k0, M - ic.m0, kv, slot);
+    tb.issue(B_KM ? B + k0 * ldb + ic.n0 : B + ic.n0 * ldb + k0, N - ic.n0, kv, slot + BM * 4);
+    if (++is == nk) {
+      is = 0;
+      ++iu;
+      if (iu < my_units) ic = unit(iu);
+    }
+  };
+
+  const int arow = wm * WM;  // wave's first row / column in the tile
+  const int bcol = wn * WN;
+  const int l32 = lane & 31;
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto read_frags = [&](int g, int ks, int buf) {
+    const uint4* slot = lds + (g % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[buf][i] = read_frag<BM, A_KM>(slot, arow + i * 32 + l32, arow + i * 32, ks, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[buf][j] = read_frag<BN, B_KM>(slot + BM * 4, bcol + j * 32 + l32, bcol + j * 32, ks, lane);
+  };
+  f32x16_t acc[TM][TN];
+  auto mfma_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  // Issue order inside a k-step: MFMA, fragment read, MFMA, read, ..., then MFMAs.
+  constexpr int kReads = (A_KM ? 2 : 1) * TM + (B_KM ? 2 : 1) * TN;
+  constexpr int kMfma = TM * TN;
+  auto interleave = [&]() {
+    constexpr int pairs = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+    for (int g = 0; g < pairs; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    if (kMfma > pairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - pairs, 0);
+    if (kReads > pairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - pairs, 0);
+  };
+
+  // Prologue: fill every slot, wait for global stage 0, fetch its first fragments.
+#pragma unroll
+  for (int s = 0; s < NS; ++s) issue_next(s);
+  vm_wait<LPS * (NS - 1)>();
+  __syncthreads();
+  read_frags(0, 0, 0);
+
+  int g = 0;  // global stage index of this workgroup
+  for (int cu = 0; cu < my_units; ++cu) {
+    const Unit cc = unit(cu);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int s = 0; s < nk; ++s, ++g) {
+      // k-step 0 of stage g, with the reads of its k-step 1 in its shadow.
+      read_frags(g, 1, 1);
+      mfma_step(0);
+      interleave();
+      // Stage g + 1 becomes visible; slot g % NS has no readers left (both of its
+      // fragment sets are in registers), so it takes stage g + NS.
+      vm_wait<LPS * (NS - 2)>();
+      __syncthreads();
+      issue_next(g % NS);
+      // k-step 1 of stage g, with the first reads of stage g + 1 in its shadow (after
+      // the last stage these read a slot that is never used: in bounds, ignored).
+      read_frags(g + 1, 0, 0);
+      mfma_step(1);
+      interleave();
+    }
+    store_acc<OUT, TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow + l32, cc.n0 + bcol, lane >> 5,
+                           OUT == kOutF32Split ? (cc.kb / kps) * split_stride : 0);
+  }
+}
+
+#define SCE_GEMM16_INST(BM, BN, WGM, AK, BK, OUT, NS, OCC)                                   \
+  template __global__ void k_gemm_bf16<BM, BN, WGM, AK, BK, OUT, NS, OCC>(                   \
+      const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
+      int64_t, int64_t, int);
+SCE_GEMM16_INST(128, 256, 2, false, false, kOutBF16, 3, 2)
+SCE_GEMM16_INST(128, 256, 2, false, true, kOutBF16, 3, 2)
+SCE_GEMM16_INST(128, 256, 2, false, true, kOutF32Split, 3, 2)
+SCE_GEMM16_INST(128, 256, 2, true, true, kOutF32Split, 3, 2)
+#undef SCE_GEMM16_INST
+
+template <int BM, int BN, int WGM, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
+static hipError_t run16(const GemmArgs& a, hipStream_t s) {
+  const int splits = a.splits > 0 ? a.splits : 1;
+  int64_t kps = (a.K + splits - 1) / splits;
+  kps = (kps + kStageK - 1) / kStageK * kStageK;
+  if (kps == 0) kps = kStageK;
+  const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
+  if (gx == 0 || gy == 0) return hipGetLastError();
+  const int64_t units = gx * gy * splits;
+  if (units > 0x7fffffff) return hipErrorInvalidValue;
+  // One workgroup per compute unit (a multiple of the 8 XCDs keeps every
+  // workgroup's units on one XCD), or one per unit when there are fewer.
+  const int slots = cu_count() * OCC;
+  const int grid = (int)(units < slots ? units : slots);
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, A_KM, B_KM, OUT, NS, OCC>), dim3((unsigned)grid),
+                     dim3(kGemmThreads), 0, s, static_cast<const bf16_t*>(a.A), a.lda,
+                     static_cast<const bf16_t*>(a.B), a.ldb, a.C, a.ldc, a.M, a.N, a.K, kps,
+                     a.split_stride, splits);
+  return hipGetLastError();
+}
+
+// Tile configuration of every bf16 product: 128 x 256 tiles, 3 LDS stages, two
+// workgroups per CU (their epilogues and stalls interleave with each other's MFMAs).
+constexpr int kTileM = 128, kTileN = 256, kOcc = 2;
+
+int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits) {
+  // Smallest k-split whose units fill at least 85% of the workgroup slots of the
+  // rounds they occupy (wave quantisation), keeping at least 1024 k per split.
+  const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
+  const int64_t slots = (int64_t)cu_count() * kOcc;
+  int best = 1;
+  double best_eff = 0.0;
+  for (int s = 1; s <= max_splits; ++s) {
+    if (s > 1 && K / s < 1024) break;
+    const int64_t units = tiles * s;
+    const int64_t rounds = (units + slots - 1) / slots;
+    const double eff = (double)units / (double)(rounds * slots);
+    if (eff >= 0.85) return s;
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
+  switch (kind) {
+    case Gemm::Logits: return run16<kTileM, kTileN, 2, false, false, kOutBF16, 3, kOcc>(a, s);
+    case Gemm::DX:
+      return a.splits > 1 ? run16<kTileM, kTileN, 2, false, true, kOutF32Split, 3, kOcc>(a, s)
+                          : run16<kTileM, kTileN, 2, false, true, kOutBF16, 3, kOcc>(a, s);
+    case Gemm::DW: return run16<kTileM, kTileN, 2, true, true, kOutF32Split, 3, kOcc>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sce

@@ -48,7 +48,11 @@ struct GemmArgs {
   int splits;            // split-K factor (DW only)
   int64_t split_stride;  // elements between split slabs of C (DW only)
 };
+// k-split factor for a GEMM of this shape (1 = no split). bf16 products only; the
+// fp32 products use gemm_dw_splits for dW and never split dX.
+int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits);
 int gemm_dw_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Gemm kind, bool bf16, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s);
 
 }  // namespace sce

@@ -58,6 +58,7 @@ def test_workspace_size_host_checks(lib):
     assert _ws(-1, 8, 100, 10, 0)[0] == 1                     # T < 0
     assert _ws(10, 8, 131073, 10, 0)[0] == 1                 # V too large for a candidate build
     assert _ws(10, 8, 1 << 20, 0, 0)[0] == 0                  # ... fine for the full softmax
+    assert _ws(10, 8, (1 << 20) + 1, 0, 0)[0] == 1            # beyond the full-softmax limit
     assert lib.sce_workspace_size(1, 8, 8, 1, 0, None) == 1   # null output pointer
 
 
