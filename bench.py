@@ -43,7 +43,36 @@ def stage_work(w, P_eff):
         "gather": ("hbm", 2.0 * w.P * w.d * es + 4 * w.P),
         # read the fp32 candidate-row gradient once, write the dense dW, read vocab_pos
         "scatter": ("hbm", P_eff * w.d * 4.0 + w.V * w.d * es + 4 * w.V),
+        # sum the fp32 k-split partials of dX into dX (bytes of a 2-way split)
+        "dx_reduce": ("hbm", 2 * w.T * w.d * 4.0 + w.T * w.d * es),
     }
+
+
+def source_sha():
+    """Hash of the HIP sources; recorded counter traffic is valid only for the same hash."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sampled_softmax_cross_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, stage):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) recorded under profiles/
+    for this workload and stage, or None when absent or taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha() or stage not in rec.get("stages", {}):
+        return None
+    s = rec["stages"][stage]
+    return int(s["fetch_bytes"] + s["write_bytes"])
 
 
 def main():
@@ -55,6 +84,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (a known-size reference "
+                         "for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sampled-CE "
@@ -139,11 +171,22 @@ def main():
         achieved = amount / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4), "traffic": None}
+                "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4),
+                "traffic": recorded_traffic(w.name, dom)}
     else:
         achieved = amount / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": recorded_traffic(w.name, dom)}
+
+    if args.calibrate_copy_mib:
+        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     full_cmp = None
     if not args.no_full_compare and w.P > 0:

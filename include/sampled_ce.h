@@ -157,9 +157,10 @@ enum {
   SCE_STAGE_LOGITS = 2,
   SCE_STAGE_CE = 3, /* CE forward/backward + loss reduction */
   SCE_STAGE_DX = 4,
-  SCE_STAGE_DW = 5,
-  SCE_STAGE_SCATTER = 6,
-  SCE_NUM_STAGES = 7
+  SCE_STAGE_DX_REDUCE = 5, /* sum of the dX k-split partials (empty when dX is not split) */
+  SCE_STAGE_DW = 6,
+  SCE_STAGE_SCATTER = 7,
+  SCE_NUM_STAGES = 8
 };
 SCE_API sce_status sce_profile_enable(int on);
 SCE_API sce_status sce_profile_collect(double* stage_ms, int nstages, int* ncalls);

@@ -229,13 +229,14 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
     if (p.dx_splits > 1) {
       GemmArgs g{Z, p.ldz, WC, d, part, d, T, d, p.Peff, p.dx_splits, T * d};
       e = launch_gemm(Gemm::DX, bf16, g, hs);
-      if (e == hipSuccess)
-        e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, bf16, dX, hs);
     } else {
       GemmArgs g{Z, p.ldz, WC, d, dX, d, T, d, p.Peff, 1, 0};
       e = launch_gemm(Gemm::DX, bf16, g, hs);
     }
   }
+  marks.mark(SCE_STAGE_DX_REDUCE);
+  if (e == hipSuccess && T > 0 && p.dx_splits > 1)
+    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, bf16, dX, hs);
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess) {
     GemmArgs g{Z, p.ldz, x, d, part, d, p.Peff, d, T, p.splits, p.Peff * d};
