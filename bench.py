@@ -49,12 +49,14 @@ def stage_work(w, P_eff):
 
 
 def source_sha():
-    """Hash of the HIP sources; recorded counter traffic is valid only for the same hash."""
+    """Hash of the kernel sources (every HIP file but the host-side ABI layer); recorded
+    counter traffic is valid only for the same hash."""
     import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sampled_softmax_cross_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+    files = glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))
+    for f in sorted(x for x in files if os.path.basename(x) != "api.hip"):
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
