@@ -40,7 +40,7 @@ def stage_work(w, P_eff):
         "dw": ("mfma", flops),
         # read Z once, write dZ once, plus labels and the row loss
         "ce": ("hbm", 2.0 * w.T * ldz * es + w.T * 12),
-        "gather": ("hbm", 2.0 * w.P * w.d * es + 4 * w.P),
+
         # read the fp32 candidate-row gradient once, write the dense dW, read vocab_pos
         "scatter": ("hbm", P_eff * w.d * 4.0 + w.V * w.d * es + 4 * w.V),
         # sum the fp32 k-split partials of dX into dX (bytes of a 2-way split)
@@ -157,7 +157,7 @@ def main():
     stages = {}
     for k, t in stage_ms.items():
         entry = {"ms": round(t, 5)}
-        if k in work and t > 0:
+        if k in work and t > 0.01:
             kind, amount = work[k]
             if kind == "mfma":
                 ach = amount / (t * 1e-3) / 1e12

@@ -129,7 +129,7 @@ SCE_API sce_status sce_build_candidates(const int64_t* targets, const int64_t* p
  *   row_lse_out [T] float32 or NULL: L_t.  row_loss_out [T] float32 or NULL: the
  *   row's loss terms before division by N.
  *   aux_out [4] int64 or NULL: as in sce_build_candidates (for P = 0: distinct
- *   targets, N, offset mod V, SCE_DEV_* bits).
+ *   targets, or -1 when V > SCE_MAX_V_SAMPLED, then N, offset mod V, SCE_DEV_* bits).
  *   workspace: at least sce_workspace_size(T, d, V, P, dtype) bytes, 256-byte aligned.
  * Inputs x, W, targets and prefix_targets are only read.
  */
@@ -152,15 +152,14 @@ SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, con
  * (HOST, may be NULL) and forgets them. Process-wide state: not thread-safe.
  */
 enum {
-  SCE_STAGE_CANDIDATES = 0, /* init, mark, build, remap */
-  SCE_STAGE_GATHER = 1,
-  SCE_STAGE_LOGITS = 2,
-  SCE_STAGE_CE = 3, /* CE forward/backward + loss reduction */
-  SCE_STAGE_DX = 4,
-  SCE_STAGE_DX_REDUCE = 5, /* sum of the dX k-split partials (empty when dX is not split) */
-  SCE_STAGE_DW = 6,
-  SCE_STAGE_SCATTER = 7,
-  SCE_NUM_STAGES = 8
+  SCE_STAGE_CANDIDATES = 0, /* candidate build, label remap and the row gather of W[C] */
+  SCE_STAGE_LOGITS = 1,
+  SCE_STAGE_CE = 2, /* CE forward/backward + loss reduction */
+  SCE_STAGE_DX = 3,
+  SCE_STAGE_DX_REDUCE = 4, /* sum of the dX k-split partials (empty when dX is not split) */
+  SCE_STAGE_DW = 5,
+  SCE_STAGE_SCATTER = 6,
+  SCE_NUM_STAGES = 7
 };
 SCE_API sce_status sce_profile_enable(int on);
 SCE_API sce_status sce_profile_collect(double* stage_ms, int nstages, int* ncalls);

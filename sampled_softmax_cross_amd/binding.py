@@ -19,7 +19,7 @@ STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
 
 EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sampled_ce_forward_backward",
            "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
-STAGES = ("candidates", "gather", "logits", "ce", "dx", "dx_reduce", "dw", "scatter")
+STAGES = ("candidates", "logits", "ce", "dx", "dx_reduce", "dw", "scatter")
 
 _lib = None
 

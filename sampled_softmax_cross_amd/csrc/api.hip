@@ -33,7 +33,7 @@ struct Plan {
   int64_t Peff = 0, ldz = 0;
   int splits = 1;     // k-split of the dW product (fp32 partials reduced by the scatter)
   int dx_splits = 1;  // k-split of the dX product (fp32 partials reduced into dX)
-  size_t counters = 0, bytemap = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
+  size_t counters = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
   size_t wc = 0, z = 0, part = 0, total = 0;
 };
 
@@ -50,7 +50,6 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     return at;
   };
   p.counters = take(kNumCounters * sizeof(int32_t));
-  p.bytemap = take((size_t)bytemap_bytes((int)V));
   p.vocab_pos = take((size_t)V * sizeof(int32_t));
   p.cand = take((size_t)(P > 0 ? P : 1) * sizeof(int32_t));
   p.tpos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
@@ -60,8 +59,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     p.wc = take(P > 0 ? (size_t)P * d * es : 0);
     p.z = take((size_t)T * p.ldz * es);
     if (dtype == SCE_BF16) {
-      p.splits = gemm_bf16_splits(p.Peff, d, T, 8);
-      p.dx_splits = gemm_bf16_splits(T, d, p.Peff, 4);
+      p.splits = gemm_bf16_splits(p.Peff, d, T, 8, false);
+      p.dx_splits = gemm_bf16_splits(T, d, p.Peff, 4, true);
     } else {
       p.splits = gemm_dw_splits(p.Peff, d, T);
     }
@@ -164,8 +163,8 @@ sce_status sce_build_candidates(const int64_t* targets, const int64_t* prefix_ta
   int32_t* vocab_pos = vocab_pos_out ? vocab_pos_out : reinterpret_cast<int32_t*>(ws + p.vocab_pos);
   int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), reinterpret_cast<uint8_t*>(ws + p.bytemap),
-                                   counters, candidates_out, vocab_pos, target_pos_out, ppos, hs);
+                                   (int)mod64(offset, V), counters, candidates_out, vocab_pos,
+                                   target_pos_out, ppos, nullptr, 0, nullptr, hs);
   if (e == hipSuccess && aux_out) e = launch_write_aux(counters, aux_out, hs);
   return hip_status(e);
 }
@@ -210,10 +209,8 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   StageMarks marks(hs);
   marks.mark(SCE_STAGE_CANDIDATES);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), reinterpret_cast<uint8_t*>(ws + p.bytemap),
-                                   counters, cand, vocab_pos, tpos, ppos, hs);
-  marks.mark(SCE_STAGE_GATHER);
-  if (e == hipSuccess && P > 0) e = launch_gather_rows(W, cand, (int)P, (int)(d * es), ws + p.wc, hs);
+                                   (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
+                                   W, (int)(d * es), ws + p.wc, hs);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
     GemmArgs g{x, d, WC, d, Z, p.ldz, T, p.Peff, d, 1, 0};
@@ -223,7 +220,6 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   if (e == hipSuccess)
     e = launch_ce_rows(Z, p.ldz, (int)T, (int)p.Peff, bf16, tpos, ppos, counters, row_loss,
                        row_lse_out, hs);
-  if (e == hipSuccess) e = launch_finalize(row_loss, (int)T, counters, loss, aux_out, hs);
   marks.mark(SCE_STAGE_DX);
   if (e == hipSuccess && T > 0) {
     if (p.dx_splits > 1) {
@@ -236,16 +232,20 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   }
   marks.mark(SCE_STAGE_DX_REDUCE);
   if (e == hipSuccess && T > 0 && p.dx_splits > 1)
-    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, bf16, dX, hs);
+    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, bf16, dX, nullptr,
+                            hs);
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess) {
     GemmArgs g{Z, p.ldz, x, d, part, d, p.Peff, d, T, p.splits, p.Peff * d};
     e = launch_gemm(Gemm::DW, bf16, g, hs);
   }
   marks.mark(SCE_STAGE_SCATTER);
-  if (e == hipSuccess)
+  if (e == hipSuccess) {
+    // The dense scatter is the last launch; its extra block also finishes the loss.
+    const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
     e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? vocab_pos : nullptr, (int)V,
-                            (int)d, bf16, dW, hs);
+                            (int)d, bf16, dW, &fin, hs);
+  }
   marks.mark(SCE_NUM_STAGES);
   return hip_status(e);
 }

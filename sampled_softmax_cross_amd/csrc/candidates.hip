@@ -3,79 +3,73 @@
 //   mark targets -> count distinct -> walk the stride window for negatives (or the
 //   page's fallback) -> ascending C and the class -> position map -> remap labels.
 //
-// The page builds C on the host with numpy; here the whole build is four small
-// kernels on the caller's stream, so the step needs no host round trip. The one
-// inherently sequential part (an ordered compaction of the window) runs in a
-// single 1024-lane workgroup with the candidate bitmap in LDS.
+// The page builds C on the host with numpy; here it is two kernels on the caller's
+// stream, so the step needs no host round trip:
+//  * k_cand: one 1024-lane workgroup with the candidate bitmap in LDS does every
+//    inherently sequential part (marking, the ordered window walk, the fallback, the
+//    ascending compaction) and clears the step's counters;
+//  * k_remap_gather: a grid kernel whose first blocks remap every label to its
+//    position and count N, and whose other blocks copy the candidates' rows of W
+//    (the gather, see gather_scatter.hip for the copy itself).
 #include "common.h"
 #include "kernels.h"
 
 namespace sce {
-
-// Zero the byte map (nbytes is a multiple of 16) and the counters.
-__global__ __launch_bounds__(256) void k_cand_init(uint4* __restrict__ bytemap, int nvec,
-                                                   int32_t* __restrict__ counters) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nvec) bytemap[i] = make_uint4(0, 0, 0, 0);
-  if (i < kNumCounters) counters[i] = 0;
-}
-
-// bytemap[y] = 1 for every target y >= 0; range check of targets and prefix targets.
-__global__ __launch_bounds__(256) void k_cand_mark(const int64_t* __restrict__ targets,
-                                                   const int64_t* __restrict__ prefix, int T,
-                                                   int V, uint8_t* __restrict__ bytemap,
-                                                   int32_t* __restrict__ counters) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  const int64_t y = targets[t];
-  bool bad = y < -1 || y >= V;
-  if (!bad && y >= 0) bytemap[y] = 1;  // racing stores all write 1
-  if (prefix != nullptr) {
-    const int64_t p = prefix[t];
-    bad |= p < -1 || p >= V;
-  }
-  if (bad) atomicOr(&counters[kStatus], kDevLabelRange);
-}
-
-// 16 bytes that are each 0 or 1 -> 16 bits.
-__device__ __forceinline__ uint32_t bytes_to_bits(uint4 q) {
-  auto four = [](uint32_t d) { return (d & 1u) | ((d >> 7) & 2u) | ((d >> 14) & 4u) | ((d >> 21) & 8u); };
-  return four(q.x) | (four(q.y) << 4) | (four(q.z) << 8) | (four(q.w) << 12);
-}
 
 __device__ __forceinline__ uint32_t valid_bits(int w, int V) {
   const int rem = V - w * 32;
   return rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
 }
 
-// One workgroup of kBuildThreads lanes. Dynamic LDS: 2 * ceil(V/32) words.
-// P == 0 only counts distinct targets (full softmax: no candidate set).
-__global__ __launch_bounds__(kBuildThreads) void k_cand_build(
-    const uint8_t* __restrict__ bytemap, int V, int P, int stride, int off,
-    int32_t* __restrict__ C, int32_t* __restrict__ vocab_pos, int32_t* __restrict__ counters) {
+// Dynamic LDS: 2 * ceil(V/32) words when mark_lds (V <= SCE_MAX_V_SAMPLED), else none.
+// P == 0 (full softmax): only the distinct count (when the bitmap fits) and the
+// label range check; C and vocab_pos are not built.
+__global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restrict__ targets,
+                                                        const int64_t* __restrict__ prefix,
+                                                        int T, int V, int P, int stride, int off,
+                                                        bool mark_lds, int32_t* __restrict__ C,
+                                                        int32_t* __restrict__ vocab_pos,
+                                                        int32_t* __restrict__ counters) {
   extern __shared__ uint32_t lds_words[];
   __shared__ int scratch[kBuildThreads / kWave + 1];
   const int W = (V + 31) >> 5;
-  uint32_t* mark = lds_words;      // candidate bitmap
-  uint32_t* aux = lds_words + W;   // window picks, then per-word prefix counts
+  uint32_t* mark = lds_words;     // candidate bitmap
+  uint32_t* aux = lds_words + W;  // window picks, then per-word prefix counts
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
 
-  // 1. byte map -> bitmap; distinct targets.
-  int cnt = 0;
-  for (int w = tid; w < W; w += nt) {
-    const uint4* src = reinterpret_cast<const uint4*>(bytemap) + 2 * w;
-    const uint32_t bits = bytes_to_bits(src[0]) | (bytes_to_bits(src[1]) << 16);
-    if (P > 0) {  // P == 0 launches without LDS: counting only
-      mark[w] = bits;
+  if (tid < kNumCounters) counters[tid] = 0;
+  if (mark_lds)
+    for (int w = tid; w < W; w += nt) {
+      mark[w] = 0;
       aux[w] = 0;
     }
-    cnt += __popc(bits);
+  __syncthreads();
+
+  // 1. Mark every class that is a target; range-check targets and prefix targets.
+  int bad = 0;
+  for (int t = tid; t < T; t += nt) {
+    const int64_t y = targets[t];
+    if (y < -1 || y >= V) {
+      bad = 1;
+    } else if (y >= 0 && mark_lds) {
+      atomicOr(&mark[y >> 5], 1u << (y & 31));
+    }
+    if (prefix != nullptr) {
+      const int64_t p = prefix[t];
+      if (p < -1 || p >= V) bad = 1;
+    }
   }
-  const int distinct = block_sum_int(cnt, scratch);  // (contains barriers)
+  __syncthreads();
+  int cnt = 0;
+  if (mark_lds)
+    for (int w = tid; w < W; w += nt) cnt += __popc(mark[w]);
+  const int distinct = block_sum_int(cnt, scratch);   // (contains barriers)
+  const int any_bad = block_sum_int(bad, scratch);
   if (P == 0) {
     if (tid == 0) {
-      counters[kDistinct] = distinct;
+      counters[kStatus] = any_bad ? kDevLabelRange : 0;
+      counters[kDistinct] = mark_lds ? distinct : -1;
       counters[kNextOffset] = off;
     }
     return;
@@ -84,7 +78,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand_build(
     // The page asserts this never happens. Flag it and leave a harmless map
     // (C = [0, P)) so that every later kernel stays in bounds.
     if (tid == 0) {
-      atomicOr(&counters[kStatus], kDevTooManyTargets);
+      counters[kStatus] = kDevTooManyTargets | (any_bad ? kDevLabelRange : 0);
       counters[kDistinct] = distinct;
       counters[kNextOffset] = off;
     }
@@ -180,19 +174,24 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand_build(
     }
   }
   if (tid == 0) {
+    counters[kStatus] = any_bad ? kDevLabelRange : 0;
     counters[kDistinct] = distinct;
     counters[kNextOffset] = next_off;
   }
 }
 
-// Labels -> positions in C (identity when P == 0); counts N.
-__global__ __launch_bounds__(256) void k_cand_remap(const int64_t* __restrict__ targets,
-                                                    const int64_t* __restrict__ prefix, int T,
-                                                    int V, int P,
-                                                    const int32_t* __restrict__ vocab_pos,
-                                                    int32_t* __restrict__ target_pos,
-                                                    int32_t* __restrict__ prefix_pos,
-                                                    int32_t* __restrict__ counters) {
+// Blocks [0, remap_blocks): labels -> positions in C (identity when P == 0), count N.
+// Blocks after that: the row gather W_C = W[C] (none when P == 0).
+__global__ __launch_bounds__(256) void k_remap_gather(
+    const int64_t* __restrict__ targets, const int64_t* __restrict__ prefix, int T, int V, int P,
+    const int32_t* __restrict__ vocab_pos, int32_t* __restrict__ target_pos,
+    int32_t* __restrict__ prefix_pos, int32_t* __restrict__ counters, int remap_blocks,
+    const uint4* __restrict__ W, const int32_t* __restrict__ C, int row_vecs,
+    uint4* __restrict__ WC) {
+  if ((int)blockIdx.x >= remap_blocks) {
+    gather_rows_block((int)blockIdx.x - remap_blocks, W, C, P, row_vecs, WC);
+    return;
+  }
   __shared__ int scratch[256 / kWave + 1];
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   int n = 0;
@@ -225,22 +224,20 @@ __global__ void k_write_aux(const int32_t* __restrict__ counters, int64_t* __res
 
 // ---------------------------------------------------------------------------
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
-                             int stride, int off, uint8_t* bytemap, int32_t* counters,
-                             int32_t* C, int32_t* vocab_pos, int32_t* target_pos,
-                             int32_t* prefix_pos, hipStream_t s) {
-  const int nvec = bytemap_bytes(V) / 16;
-  const int init_threads = nvec > kNumCounters ? nvec : kNumCounters;
-  hipLaunchKernelGGL(k_cand_init, dim3((init_threads + 255) / 256), dim3(256), 0, s,
-                     reinterpret_cast<uint4*>(bytemap), nvec, counters);
-  if (T > 0)
-    hipLaunchKernelGGL(k_cand_mark, dim3((T + 255) / 256), dim3(256), 0, s, targets, prefix, T,
-                       V, bytemap, counters);
-  const size_t lds = P > 0 ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
-  hipLaunchKernelGGL(k_cand_build, dim3(1), dim3(kBuildThreads), lds, s, bytemap, V, P, stride,
-                     off, C, vocab_pos, counters);
-  if (T > 0)
-    hipLaunchKernelGGL(k_cand_remap, dim3((T + 255) / 256), dim3(256), 0, s, targets, prefix, T,
-                       V, P, vocab_pos, target_pos, prefix_pos, counters);
+                             int stride, int off, int32_t* counters, int32_t* C,
+                             int32_t* vocab_pos, int32_t* target_pos, int32_t* prefix_pos,
+                             const void* W, int row_bytes, void* WC, hipStream_t s) {
+  const bool mark_lds = V <= kMaxBitmapClasses;
+  const size_t lds = mark_lds ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
+  hipLaunchKernelGGL(k_cand, dim3(1), dim3(kBuildThreads), lds, s, targets, prefix, T, V, P,
+                     stride, off, mark_lds, C, vocab_pos, counters);
+  const int remap_blocks = (T + 255) / 256;
+  const int gather_blocks = (W != nullptr && P > 0) ? gather_block_count(P, row_bytes / 16) : 0;
+  if (remap_blocks + gather_blocks > 0)
+    hipLaunchKernelGGL(k_remap_gather, dim3(remap_blocks + gather_blocks), dim3(256), 0, s,
+                       targets, prefix, T, V, P, vocab_pos, target_pos, prefix_pos, counters,
+                       remap_blocks, reinterpret_cast<const uint4*>(W), C, row_bytes / 16,
+                       reinterpret_cast<uint4*>(WC));
   return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@
 // never re-reads Z and allocates no second [T, P] buffer. Each lane keeps its
 // slice of the row as exp(Z - m_lane) after the first sweep, so the gradient
 // costs one multiply per element; lanes merge their (max, sum) pairs with the
-// online-softmax rule (rescale the smaller-max sum by exp(m_small - m_big)).
+// online-softmax rule (rescale the smaller-max sum by exp(m_small - m_big)). The
+// rows' loss terms are summed by the last kernel of the step (the dense scatter).
 #include "common.h"
 #include "kernels.h"
 
@@ -239,19 +240,22 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
 
 template <typename TZ, int NT, int VPT>
 static void launch_ce_fixed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp, const int32_t* pp,
-                            const int32_t* counters, float* rl, float* lse, hipStream_t s) {
-  hipLaunchKernelGGL((k_ce_rows<TZ, NT, VPT>), dim3(T), dim3(NT), 0, s, Z, ldz, P, tp, pp, counters,
-                     rl, lse);
+                            int32_t* counters, float* rl, float* lse, float* loss, int64_t* aux,
+                            hipStream_t s) {
+  (void)loss;
+  (void)aux;
+  hipLaunchKernelGGL((k_ce_rows<TZ, NT, VPT>), dim3(T), dim3(NT), 0, s, Z, ldz, P, tp, pp,
+                     counters, rl, lse);
 }
 
 template <typename TZ, int NT>
 static bool launch_ce_nt(int vpt, TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
-                         const int32_t* pp, const int32_t* counters, float* rl, float* lse,
-                         hipStream_t s) {
+                         const int32_t* pp, int32_t* counters, float* rl, float* lse, float* loss,
+                         int64_t* aux, hipStream_t s) {
   switch (vpt) {
 #define SCE_CE_CASE(n) \
   case n:              \
-    launch_ce_fixed<TZ, NT, n>(Z, ldz, T, P, tp, pp, counters, rl, lse, s); \
+    launch_ce_fixed<TZ, NT, n>(Z, ldz, T, P, tp, pp, counters, rl, lse, loss, aux, s); \
     return true;
     SCE_CE_CASE(1) SCE_CE_CASE(2) SCE_CE_CASE(3) SCE_CE_CASE(4) SCE_CE_CASE(5) SCE_CE_CASE(6)
     SCE_CE_CASE(7) SCE_CE_CASE(8) SCE_CE_CASE(9) SCE_CE_CASE(10) SCE_CE_CASE(11) SCE_CE_CASE(12)
@@ -264,17 +268,19 @@ static bool launch_ce_nt(int vpt, TZ* Z, int64_t ldz, int T, int P, const int32_
 
 template <typename TZ>
 static void launch_ce_typed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
-                            const int32_t* pp, const int32_t* counters, float* rl, float* lse,
-                            hipStream_t s) {
+                            const int32_t* pp, int32_t* counters, float* rl, float* lse,
+                            float* loss, int64_t* aux, hipStream_t s) {
   constexpr int E = RowVec<TZ>::kElems;
   const int64_t nvec = ldz / E;
   if (nvec <= 256 * 16) {
-    launch_ce_nt<TZ, 256>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse, s);
+    launch_ce_nt<TZ, 256>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse,
+                          loss, aux, s);
   } else if (nvec <= 512 * 16) {
-    launch_ce_nt<TZ, 512>((int)((nvec + 511) / 512), Z, ldz, T, P, tp, pp, counters, rl, lse, s);
+    launch_ce_nt<TZ, 512>((int)((nvec + 511) / 512), Z, ldz, T, P, tp, pp, counters, rl, lse,
+                          loss, aux, s);
   } else {
-    hipLaunchKernelGGL((k_ce_rows_stream<TZ, 1024>), dim3(T), dim3(1024), 0, s, Z, ldz, P, tp, pp,
-                       counters, rl, lse);
+    hipLaunchKernelGGL((k_ce_rows_stream<TZ, 1024>), dim3(T), dim3(1024), 0, s, Z, ldz, P, tp,
+                       pp, counters, rl, lse);
   }
 }
 
@@ -284,47 +290,11 @@ hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
                           hipStream_t s) {
   if (T <= 0) return hipGetLastError();
   if (bf16)
-    launch_ce_typed<bf16_t>(static_cast<bf16_t*>(Z), ldz, T, P, target_pos, prefix_pos, counters,
-                            row_loss, row_lse, s);
+    launch_ce_typed<bf16_t>(static_cast<bf16_t*>(Z), ldz, T, P, target_pos, prefix_pos,
+                            const_cast<int32_t*>(counters), row_loss, row_lse, nullptr, nullptr, s);
   else
-    launch_ce_typed<float>(static_cast<float*>(Z), ldz, T, P, target_pos, prefix_pos, counters,
-                           row_loss, row_lse, s);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// loss = sum_t row_loss[t] / N, summed in a fixed order (deterministic).
-constexpr int kFinalizeThreads = 1024;
-
-__global__ __launch_bounds__(kFinalizeThreads) void k_finalize(const float* __restrict__ row_loss,
-                                                               int T,
-                                                               const int32_t* __restrict__ counters,
-                                                               float* __restrict__ loss,
-                                                               int64_t* __restrict__ aux) {
-  __shared__ double red[kFinalizeThreads / kWave];
-  double acc = 0.0;
-  for (int t = threadIdx.x; t < T; t += kFinalizeThreads) acc += (double)row_loss[t];
-  acc = wave_sum(acc);
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int w = 0; w < kFinalizeThreads / kWave; ++w) tot += red[w];
-    const int N = counters[kNumLabels];
-    *loss = N > 0 ? (float)(tot / (double)N) : 0.f;
-    if (aux) {
-      aux[0] = counters[kDistinct];
-      aux[1] = N;
-      aux[2] = counters[kNextOffset];
-      aux[3] = counters[kStatus];
-    }
-  }
-}
-
-hipError_t launch_finalize(const float* row_loss, int T, const int32_t* counters, float* loss,
-                           int64_t* aux, hipStream_t s) {
-  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kFinalizeThreads), 0, s, row_loss, T, counters, loss,
-                     aux);
+    launch_ce_typed<float>(static_cast<float*>(Z), ldz, T, P, target_pos, prefix_pos,
+                           const_cast<int32_t*>(counters), row_loss, row_lse, nullptr, nullptr, s);
   return hipGetLastError();
 }
 

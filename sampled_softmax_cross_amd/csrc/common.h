@@ -14,6 +14,7 @@ enum Counter : int {
   kNumLabels = 1,  // N: labels whose position is >= 0
   kDistinct = 2,   // distinct targets
   kNextOffset = 3, // sweep offset after the build
+  kCeDone = 4,     // CE rows finished (the last one reduces the loss)
   kNumCounters = 8
 };
 constexpr int kDevTooManyTargets = 1;

@@ -1,4 +1,5 @@
-// Row gather W_C = W[C] and the dense scatter of the candidate-row gradient.
+// The dense scatter of the candidate-row gradient (the row gather lives in
+// kernels.h and runs inside the remap launch).
 //
 // Both are pure data movement ("sampled_softmax.py", SampledSoftmax._gather_rows
 // copies the candidates' lm_head rows into a contiguous [P, d] table; the module
@@ -14,50 +15,56 @@
 namespace sce {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
 
-__global__ __launch_bounds__(kCopyThreads) void k_gather_rows(const uint4* __restrict__ W,
-                                                              const int32_t* __restrict__ C,
-                                                              int P, int row_vecs,
-                                                              uint4* __restrict__ WC) {
-  const int total = P * row_vecs;
-  const int base = blockIdx.x * (kCopyThreads * kCopyUnroll) + threadIdx.x;
-  uint4 v[kCopyUnroll];
+// loss = sum of the rows' loss terms / N, summed by one block in a fixed order.
+__device__ void finish_loss(const LossOut& f) {
+  __shared__ double part[kCopyThreads / kWave];
+  // Eight independent partial sums per lane keep eight loads in flight; lane l adds
+  // rows l + 256 (8k + j) into partial j, and the partials are added in order j.
+  constexpr int kAcc = 8;
+  double a[kAcc] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int t0 = threadIdx.x; t0 < f.T; t0 += kCopyThreads * kAcc) {
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int i = base + u * kCopyThreads;
-    if (i < total) {
-      const int r = i / row_vecs;
-      const int k = i - r * row_vecs;
-      v[u] = W[(int64_t)C[r] * row_vecs + k];
+    for (int j = 0; j < kAcc; ++j) {
+      const int t = t0 + j * kCopyThreads;
+      if (t < f.T) a[j] += (double)f.row_loss[t];
     }
   }
+  double acc = 0.0;
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int i = base + u * kCopyThreads;
-    if (i < total) WC[i] = v[u];
+  for (int j = 0; j < kAcc; ++j) acc += a[j];
+  acc = wave_sum(acc);
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kCopyThreads / kWave; ++w) tot += part[w];
+    const int N = f.counters[kNumLabels];
+    *f.loss = N > 0 ? (float)(tot / (double)N) : 0.f;
+    if (f.aux) {
+      f.aux[0] = f.counters[kDistinct];
+      f.aux[1] = N;
+      f.aux[2] = f.counters[kNextOffset];
+      f.aux[3] = f.counters[kStatus];
+    }
   }
 }
 
-hipError_t launch_gather_rows(const void* W, const int32_t* C, int P, int row_bytes, void* WC,
-                              hipStream_t s) {
-  const int row_vecs = row_bytes / 16;
-  const int64_t total = (int64_t)P * row_vecs;
-  const int blocks = (int)((total + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll));
-  if (blocks > 0)
-    hipLaunchKernelGGL(k_gather_rows, dim3(blocks), dim3(kCopyThreads), 0, s,
-                       reinterpret_cast<const uint4*>(W), C, P, row_vecs,
-                       reinterpret_cast<uint4*>(WC));
-  return hipGetLastError();
-}
-
-// Each lane produces 8 consecutive output elements of one dense row.
+// Each lane produces 8 consecutive output elements of one dense row. With a LossOut,
+// block 0 finishes the loss (alongside the copy) and the copy uses blocks 1...
 template <bool BF16>
 __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
     const float* __restrict__ part, int splits, int64_t split_stride,
-    const int32_t* __restrict__ vocab_pos, int V, int d, void* __restrict__ dW) {
+    const int32_t* __restrict__ vocab_pos, int V, int d, void* __restrict__ dW, int copy_blocks,
+    LossOut fin) {
+  const int first = (int)gridDim.x - copy_blocks;  // 1 with a LossOut, else 0
+  if ((int)blockIdx.x < first) {
+    finish_loss(fin);
+    return;
+  }
   const int vecs_per_row = d / 8;
-  const int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+  const int64_t i = (int64_t)(blockIdx.x - first) * kCopyThreads + threadIdx.x;
   if (i >= (int64_t)V * vecs_per_row) return;
   const int v = (int)(i / vecs_per_row);
   const int c8 = (int)(i - (int64_t)v * vecs_per_row);
@@ -88,16 +95,18 @@ __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
 
 hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stride,
                                const int32_t* vocab_pos, int V, int d, bool bf16, void* dW,
-                               hipStream_t s) {
+                               const LossOut* fin, hipStream_t s) {
   const int64_t total = (int64_t)V * (d / 8);
   const int blocks = (int)((total + kCopyThreads - 1) / kCopyThreads);
-  if (blocks > 0) {
+  const LossOut f = fin ? *fin : LossOut{nullptr, 0, nullptr, nullptr, nullptr};
+  const int grid = blocks + (fin ? 1 : 0);
+  if (grid > 0) {
     if (bf16)
-      hipLaunchKernelGGL(k_scatter_rows<true>, dim3(blocks), dim3(kCopyThreads), 0, s, part,
-                         splits, split_stride, vocab_pos, V, d, dW);
+      hipLaunchKernelGGL(k_scatter_rows<true>, dim3(grid), dim3(kCopyThreads), 0, s, part, splits,
+                         split_stride, vocab_pos, V, d, dW, blocks, f);
     else
-      hipLaunchKernelGGL(k_scatter_rows<false>, dim3(blocks), dim3(kCopyThreads), 0, s, part,
-                         splits, split_stride, vocab_pos, V, d, dW);
+      hipLaunchKernelGGL(k_scatter_rows<false>, dim3(grid), dim3(kCopyThreads), 0, s, part,
+                         splits, split_stride, vocab_pos, V, d, dW, blocks, f);
   }
   return hipGetLastError();
 }

@@ -54,11 +54,12 @@ __device__ __forceinline__ int km_index(int k, int ch) {
   return k * (R / 8) + (ch ^ ((k & 3) << 2));
 }
 
-// One operand tile of R rows (r-major) or R columns (k-major) per stage.
-template <int R, bool KMAJ>
+// One operand tile of R rows (r-major) or R columns (k-major) per stage, filled by
+// NW waves.
+template <int R, bool KMAJ, int NW>
 struct DmaTile {
-  static_assert(R % 64 == 0 && (!KMAJ || R % 128 == 0), "tile shape");
-  static constexpr int kN = R / 64;  // DMA instructions per wave per stage
+  static_assert(R % (16 * NW) == 0 && (!KMAJ || R % 128 == 0), "tile shape");
+  static constexpr int kN = R / (16 * NW);  // DMA instructions per wave per stage
   int off[kN];  // byte offset of the lane's chunk from the tile origin
   int kk[kN];   // k of the lane's chunk (r-major) or row (k-major), for the k clip
   int rr[kN];   // row (r-major) or first column (k-major) of the lane's chunk
@@ -124,17 +125,17 @@ __device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int
 // u = blockIdx.x, blockIdx.x + gridDim.x, ... and streams their k-stages through one
 // NS-deep LDS ring without a break between units: the first stages of the next unit
 // are already in flight while the current unit finishes and stores its tile.
-// BM x BN tile per unit, 4 waves as WGM x (4 / WGM); OCC workgroups share a CU.
-template <int BM, int BN, int WGM, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
-__global__ __launch_bounds__(kGemmThreads, OCC) void k_gemm_bf16(
+// BM x BN tile per unit, WGM x WGN waves; OCC workgroups share a CU.
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ Cout, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t kps,
     int64_t split_stride, int splits) {
-  constexpr int WGN = 4 / WGM;
+  constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int STAGE = (BM + BN) * 4;  // uint4 per stage (64 B per row/column)
-  constexpr int LPS = BM / 64 + BN / 64;  // DMA instructions per wave per stage
+  constexpr int LPS = (BM + BN) / (16 * NW);  // DMA instructions per wave per stage
   static_assert(NS >= 3 && LPS * (NS - 1) < 64, "pipeline depth");
   __shared__ uint4 lds[NS * STAGE];
 
@@ -165,8 +166,8 @@ __global__ __launch_bounds__(kGemmThreads, OCC) void k_gemm_bf16(
     return c;
   };
 
-  DmaTile<BM, A_KM> ta;
-  DmaTile<BN, B_KM> tb;
+  DmaTile<BM, A_KM, NW> ta;
+  DmaTile<BN, B_KM, NW> tb;
   ta.init(lda);
   tb.init(ldb);
   // Issue cursor: unit iu, stage is of that unit. Past the last unit, stages are
@@ -259,17 +260,17 @@ __global__ __launch_bounds__(kGemmThreads, OCC) void k_gemm_bf16(
   }
 }
 
-#define SCE_GEMM16_INST(BM, BN, WGM, AK, BK, OUT, NS, OCC)                                   \
-  template __global__ void k_gemm_bf16<BM, BN, WGM, AK, BK, OUT, NS, OCC>(                   \
+#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC)                              \
+  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC>(              \
       const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
       int64_t, int64_t, int);
-SCE_GEMM16_INST(128, 256, 2, false, false, kOutBF16, 3, 2)
-SCE_GEMM16_INST(128, 256, 2, false, true, kOutBF16, 3, 2)
-SCE_GEMM16_INST(128, 256, 2, false, true, kOutF32Split, 3, 2)
-SCE_GEMM16_INST(128, 256, 2, true, true, kOutF32Split, 3, 2)
+SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 3, 1)
+SCE_GEMM16_INST(128, 256, 2, 2, false, true, kOutBF16, 3, 2)
+SCE_GEMM16_INST(128, 256, 2, 2, false, true, kOutF32Split, 3, 2)
+SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2)
 #undef SCE_GEMM16_INST
 
-template <int BM, int BN, int WGM, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
 static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   const int splits = a.splits > 0 ? a.splits : 1;
   int64_t kps = (a.K + splits - 1) / splits;
@@ -283,22 +284,28 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   // workgroup's units on one XCD), or one per unit when there are fewer.
   const int slots = cu_count() * OCC;
   const int grid = (int)(units < slots ? units : slots);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, A_KM, B_KM, OUT, NS, OCC>), dim3((unsigned)grid),
-                     dim3(kGemmThreads), 0, s, static_cast<const bf16_t*>(a.A), a.lda,
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC>),
+                     dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, s, static_cast<const bf16_t*>(a.A), a.lda,
                      static_cast<const bf16_t*>(a.B), a.ldb, a.C, a.ldc, a.M, a.N, a.K, kps,
                      a.split_stride, splits);
   return hipGetLastError();
 }
 
-// Tile configuration of every bf16 product: 128 x 256 tiles, 3 LDS stages, two
-// workgroups per CU (their epilogues and stalls interleave with each other's MFMAs).
+// Tile configurations (measured on MI355X with random bf16 inputs at the workload
+// shapes): the logits product uses 256 x 256 tiles with 8 waves (2 x 4, 128 x 64 each,
+// two waves per SIMD) and one workgroup per CU; dX and dW use 128 x 256 tiles with 4
+// waves and two workgroups per CU (their epilogues and stalls interleave). Three LDS
+// stages each.
 constexpr int kTileM = 128, kTileN = 256, kOcc = 2;
 
-int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits) {
+int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass) {
   // Smallest k-split whose units fill at least 85% of the workgroup slots of the
-  // rounds they occupy (wave quantisation), keeping at least 1024 k per split.
+  // rounds they occupy (wave quantisation), keeping at least 1024 k per split. When a
+  // split needs an extra reduction pass (dX), it is only taken once the unsplit
+  // product already fills a full round of slots.
   const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
   const int64_t slots = (int64_t)cu_count() * kOcc;
+  if (split_costs_pass && tiles < slots) return 1;
   int best = 1;
   double best_eff = 0.0;
   for (int s = 1; s <= max_splits; ++s) {
@@ -317,11 +324,11 @@ int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits) {
 
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {
-    case Gemm::Logits: return run16<kTileM, kTileN, 2, false, false, kOutBF16, 3, kOcc>(a, s);
+    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 3, 1>(a, s);
     case Gemm::DX:
-      return a.splits > 1 ? run16<kTileM, kTileN, 2, false, true, kOutF32Split, 3, kOcc>(a, s)
-                          : run16<kTileM, kTileN, 2, false, true, kOutBF16, 3, kOcc>(a, s);
-    case Gemm::DW: return run16<kTileM, kTileN, 2, true, true, kOutF32Split, 3, kOcc>(a, s);
+      return a.splits > 1 ? run16<kTileM, kTileN, 2, 2, false, true, kOutF32Split, 3, kOcc>(a, s)
+                          : run16<kTileM, kTileN, 2, 2, false, true, kOutBF16, 3, kOcc>(a, s);
+    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -7,33 +7,66 @@
 namespace sce {
 
 constexpr int kBuildThreads = 1024;
+// Largest vocabulary whose candidate bitmaps (2 x V bits) the build keeps in LDS.
+constexpr int kMaxBitmapClasses = 131072;
 
-// Byte map of candidate marks: one byte per class, rounded up to 32 classes.
-inline int bytemap_bytes(int V) { return (V + 31) / 32 * 32; }
-
+// Candidate build (P > 0) or label check (P == 0), then the label remap and, when W
+// is given and P > 0, the row gather W_C = W[C] (rows of row_bytes, a multiple of 16).
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
-                             int stride, int off, uint8_t* bytemap, int32_t* counters,
-                             int32_t* C, int32_t* vocab_pos, int32_t* target_pos,
-                             int32_t* prefix_pos, hipStream_t s);
+                             int stride, int off, int32_t* counters, int32_t* C,
+                             int32_t* vocab_pos, int32_t* target_pos, int32_t* prefix_pos,
+                             const void* W, int row_bytes, void* WC, hipStream_t s);
 hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s);
 
-// W_C[i, :] = W[C[i], :] (rows of row_bytes, a multiple of 16).
-hipError_t launch_gather_rows(const void* W, const int32_t* C, int P, int row_bytes, void* WC,
-                              hipStream_t s);
+// Row gather, one block of 256 lanes per kGatherRows rows: 32 lanes per row, each
+// moving whole 16-byte vectors, every load of a lane issued before its stores.
+constexpr int kGatherRows = 8;
+inline int gather_block_count(int P, int row_vecs) {
+  (void)row_vecs;
+  return (P + kGatherRows - 1) / kGatherRows;
+}
+__device__ __forceinline__ void gather_rows_block(int blk, const uint4* __restrict__ W,
+                                                  const int32_t* __restrict__ C, int P,
+                                                  int row_vecs, uint4* __restrict__ WC) {
+  const int r = blk * kGatherRows + (int)(threadIdx.x >> 5);
+  if (r >= P) return;
+  const int l = threadIdx.x & 31;
+  const uint4* src = W + (int64_t)C[r] * row_vecs;
+  uint4* dst = WC + (int64_t)r * row_vecs;
+  for (int v0 = l; v0 < row_vecs; v0 += 32 * 4) {
+    const bool k1 = v0 + 32 < row_vecs, k2 = v0 + 64 < row_vecs, k3 = v0 + 96 < row_vecs;
+    uint4 b1 = make_uint4(0, 0, 0, 0), b2 = b1, b3 = b1;
+    const uint4 b0 = src[v0];
+    if (k1) b1 = src[v0 + 32];
+    if (k2) b2 = src[v0 + 64];
+    if (k3) b3 = src[v0 + 96];
+    dst[v0] = b0;
+    if (k1) dst[v0 + 32] = b1;
+    if (k2) dst[v0 + 64] = b2;
+    if (k3) dst[v0 + 96] = b3;
+  }
+}
 // dW[v, :] = sum over splits of part[s, pos(v), :] (fp32) in dtype, or 0 when pos(v) < 0;
-// pos = vocab_pos, or the identity when vocab_pos is null.
+// pos = vocab_pos, or the identity when vocab_pos is null. When `loss` is given, the
+// launch also finishes the step's scalars: loss = sum(row_loss[0..T)) / N in a fixed
+// order (0 when N == 0) and, when aux is given, the counters.
+struct LossOut {
+  const float* row_loss;
+  int T;
+  const int32_t* counters;
+  float* loss;
+  int64_t* aux;
+};
 hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stride,
                                const int32_t* vocab_pos, int V, int d, bool bf16, void* dW,
-                               hipStream_t s);
+                               const LossOut* fin, hipStream_t s);
 
 // Row-wise cross-entropy forward/backward over Z [T, ldz] (P valid columns), in place.
 hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
                           const int32_t* target_pos, const int32_t* prefix_pos,
                           const int32_t* counters, float* row_loss, float* row_lse,
                           hipStream_t s);
-// loss = sum(row_loss) / N (0 when N == 0); optional aux copy.
-hipError_t launch_finalize(const float* row_loss, int T, const int32_t* counters, float* loss,
-                           int64_t* aux, hipStream_t s);
+
 
 // GEMMs. Matrices row-major; see gemm.hip for the operand conventions.
 enum class Gemm { Logits, DX, DW };
@@ -50,7 +83,7 @@ struct GemmArgs {
 };
 // k-split factor for a GEMM of this shape (1 = no split). bf16 products only; the
 // fp32 products use gemm_dw_splits for dW and never split dX.
-int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits);
+int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass);
 int gemm_dw_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Gemm kind, bool bf16, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s);
