@@ -62,6 +62,7 @@ typedef enum sce_dtype { SCE_F32 = 0, SCE_BF16 = 1 } sce_dtype;
 #define SCE_MAX_V_SAMPLED 131072 /* V limit when P > 0 (two candidate bitmaps held in LDS) */
 #define SCE_MAX_V 1048576        /* V limit for the full softmax (32-bit tile offsets) */
 #define SCE_MAX_D 16384
+#define SCE_MAX_TD (1LL << 34)   /* T * d limit (32-bit 8-element vector indexes over x and dX) */
 
 /*
  * sce_workspace_size -- bytes of device workspace a call with these sizes needs.

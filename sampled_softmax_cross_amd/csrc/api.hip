@@ -81,6 +81,7 @@ sce_status check_sizes(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bo
   if (P < 0 || P > V) return SCE_EINVAL;
   if (P > 0 && V > SCE_MAX_V_SAMPLED) return SCE_EINVAL;
   if (need_d && (d < 8 || d % 8 != 0 || d > SCE_MAX_D)) return SCE_EINVAL;
+  if (need_d && T * d > SCE_MAX_TD) return SCE_EINVAL;
   if (dtype != SCE_F32 && dtype != SCE_BF16) return SCE_EINVAL;
   return SCE_OK;
 }

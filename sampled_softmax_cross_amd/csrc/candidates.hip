@@ -47,17 +47,26 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
   __syncthreads();
 
   // 1. Mark every class that is a target; range-check targets and prefix targets.
+  //    Each lane loads kMarkLoads labels before it uses any, so one workgroup keeps
+  //    enough loads in flight to stream the label arrays.
+  constexpr int kMarkLoads = 8;
   int bad = 0;
-  for (int t = tid; t < T; t += nt) {
-    const int64_t y = targets[t];
-    if (y < -1 || y >= V) {
-      bad = 1;
-    } else if (y >= 0 && mark_lds) {
-      atomicOr(&mark[y >> 5], 1u << (y & 31));
+  for (int t0 = tid; t0 < T; t0 += nt * kMarkLoads) {
+    int64_t y[kMarkLoads], q[kMarkLoads];
+#pragma unroll
+    for (int j = 0; j < kMarkLoads; ++j) {
+      const int t = t0 + j * nt;
+      y[j] = t < T ? targets[t] : -1;
+      q[j] = (prefix != nullptr && t < T) ? prefix[t] : -1;
     }
-    if (prefix != nullptr) {
-      const int64_t p = prefix[t];
-      if (p < -1 || p >= V) bad = 1;
+#pragma unroll
+    for (int j = 0; j < kMarkLoads; ++j) {
+      if (y[j] < -1 || y[j] >= V) {
+        bad = 1;
+      } else if (y[j] >= 0 && mark_lds) {
+        atomicOr(&mark[y[j] >> 5], 1u << (y[j] & 31));
+      }
+      if (q[j] < -1 || q[j] >= V) bad = 1;
     }
   }
   __syncthreads();
@@ -162,6 +171,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
     }
   }
   __syncthreads();
+#pragma unroll 4
   for (int c = tid; c < V; c += nt) {
     const uint32_t m = mark[c >> 5];
     const int b = c & 31;

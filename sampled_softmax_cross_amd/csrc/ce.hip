@@ -10,8 +10,8 @@
 //
 // The row is read from HBM once into registers and written once: the kernel
 // never re-reads Z and allocates no second [T, P] buffer. Each lane keeps its
-// slice of the row as exp(Z - m_lane) after the first sweep, so the gradient
-// costs one multiply per element; lanes merge their (max, sum) pairs with the
+// slice of the row as loaded and sweeps it twice (max and sum of exp(Z - m_lane),
+// then exp(Z - L) for the gradient); lanes merge their (max, sum) pairs with the
 // online-softmax rule (rescale the smaller-max sum by exp(m_small - m_big)). The
 // rows' loss terms are summed by the last kernel of the step (the dense scatter).
 #include "common.h"
@@ -84,6 +84,15 @@ __device__ __forceinline__ void block_merge_ms(float& m, float& s, float* red) {
   s = S;
 }
 
+// Hides the packed row from the optimiser between sweeps, so that each sweep unpacks
+// it again instead of keeping every unpacked value live (which would double the
+// registers a row needs).
+template <int VPT>
+__device__ __forceinline__ void opaque(uint4 (&q)[VPT]) {
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) asm volatile("" : "+v"(q[k].x), "+v"(q[k].y), "+v"(q[k].z), "+v"(q[k].w));
+}
+
 // Register-resident row: NT lanes x VPT vectors of 16 bytes cover the row.
 template <typename TZ, int NT, int VPT>
 __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz, int P,
@@ -107,34 +116,78 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
     zlab[1] = pp >= 0 ? RV::load1(row + pp) : 0.f;
   }
 
-  float v[VPT][E];
+  // The row stays in registers as loaded. Short rows (up to 40 values per lane) keep
+  // exp(Z - m_lane) per element after the first sweep, so the gradient costs one
+  // multiply (the kernel is close to ALU-bound there); long rows
+  // keep only the packed 16-byte vectors (half the registers for bf16, so more rows
+  // per CU keep loads in flight) and evaluate the exponential a second time.
+  // Only the last vector of a row can hold padding columns (j >= P).
+  constexpr bool kKeep = VPT * E <= 40;
+  uint4 q[kKeep ? 1 : VPT];
+  float v[kKeep ? VPT : 1][E];
   float m = -INFINITY;
+  float s = 0.f;
+  if constexpr (kKeep) {
+    // Unpack at load (padding and vectors past the row become -inf), then replace each
+    // value by exp(Z - m_lane).
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int i = threadIdx.x + k * NT;
-    if (i < nvec) {
-      const uint4 q = rowv[i];
-      RV::unpack(q, v[k]);
+    for (int k = 0; k < VPT; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < nvec) {
+        RV::unpack(rowv[i], v[k]);
+        if ((i + 1) * E > P) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (i * E + e >= P) v[k][e] = -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[k][e] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) m = fmaxf(m, v[k][e]);
+    }
+    const float mb = m == -INFINITY ? 0.f : m * kLog2e;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        if (i * E + e >= P) v[k][e] = -INFINITY;
-        m = fmaxf(m, v[k][e]);
+        v[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][e], kLog2e, -mb));  // exp2(-inf) = 0
+        s += v[k][e];
       }
-    } else {
+  } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[k][e] = -INFINITY;
+    for (int k = 0; k < VPT; ++k) {
+      const int i = threadIdx.x + k * NT;
+      q[k] = i < nvec ? rowv[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < nvec) {
+        float f[E];
+        RV::unpack(q[k], f);
+        const bool full = (i + 1) * E <= P;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (full || i * E + e < P) m = fmaxf(m, f[e]);
+      }
+    }
+    const float mb = m == -INFINITY ? 0.f : m * kLog2e;
+    opaque(q);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < nvec) {
+        float f[E];
+        RV::unpack(q[k], f);
+        const bool full = (i + 1) * E <= P;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (full || i * E + e < P) s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], kLog2e, -mb));
+      }
     }
   }
-  // exp(Z - m_lane), kept for the gradient; exp2 of -inf is exactly 0.
-  float s = 0.f;
-  const float mb = m == -INFINITY ? 0.f : m * kLog2e;
-#pragma unroll
-  for (int k = 0; k < VPT; ++k)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      v[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][e], kLog2e, -mb));
-      s += v[k][e];
-    }
   float M = m, S = s;
   block_merge_ms<NT>(M, S, red);
   const float L = M + __builtin_amdgcn_logf(S) * kLn2;  // logf here is log2
@@ -142,18 +195,31 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
   const int N = counters[kNumLabels];
   const float inv = N > 0 ? 1.0f / (float)N : 0.f;
   const int nt = (tp >= 0) + (pp >= 0);
-  // exp(Z - L) = exp(Z - m_lane) * exp(m_lane - L)
-  const float scale = m == -INFINITY ? 0.f
-                                     : (float)nt * inv * __builtin_amdgcn_exp2f((m - L) * kLog2e);
+  // kKeep: exp(Z - L) = exp(Z - m_lane) * exp(m_lane - L); else exp(Z - L) directly.
+  const float scale = kKeep ? (m == -INFINITY ? 0.f : (float)nt * inv * __builtin_amdgcn_exp2f((m - L) * kLog2e))
+                            : (float)nt * inv;
+  const float Lb = L * kLog2e;
   const int vt = tp >= 0 ? tp / E : -1;
   const int vp = pp >= 0 ? pp / E : -1;
+  if constexpr (!kKeep) opaque(q);
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int i = threadIdx.x + k * NT;
     if (i < nvec) {
       float g[E];
+      if constexpr (kKeep) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) g[e] = v[k][e] * scale;  // 0 on padding columns
+        for (int e = 0; e < E; ++e) g[e] = v[k][e] * scale;  // 0 on padding columns
+      } else {
+        float f[E];
+        RV::unpack(q[k], f);
+        const bool full = (i + 1) * E <= P;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], kLog2e, -Lb)) * scale;
+          g[e] = (full || i * E + e < P) ? x : 0.f;
+        }
+      }
       if (i == vt || i == vp) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {

@@ -51,8 +51,11 @@ __device__ void finish_loss(const LossOut& f) {
   }
 }
 
-// Each lane produces 8 consecutive output elements of one dense row. With a LossOut,
-// block 0 finishes the loss (alongside the copy) and the copy uses blocks 1...
+// Each lane produces kScatterVecs vectors of 8 consecutive output elements, spaced a
+// block apart so that every load of a lane is issued before its first store. With a
+// LossOut, block 0 finishes the loss (alongside the copy) and the copy uses blocks 1...
+// Flat vector indexes fit 32 bits: V * d / 8 <= 2^31 by the library's size limits.
+constexpr int kScatterVecs = 4;
 template <bool BF16>
 __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
     const float* __restrict__ part, int splits, int64_t split_stride,
@@ -63,33 +66,61 @@ __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
     finish_loss(fin);
     return;
   }
-  const int vecs_per_row = d / 8;
-  const int64_t i = (int64_t)(blockIdx.x - first) * kCopyThreads + threadIdx.x;
-  if (i >= (int64_t)V * vecs_per_row) return;
-  const int v = (int)(i / vecs_per_row);
-  const int c8 = (int)(i - (int64_t)v * vecs_per_row);
-  const int p = vocab_pos ? vocab_pos[v] : v;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (p >= 0) {
-    const float* src = part + (int64_t)p * d + c8 * 8;
-    for (int sidx = 0; sidx < splits; ++sidx) {
-      const float4 a = *reinterpret_cast<const float4*>(src + sidx * split_stride);
-      const float4 b = *reinterpret_cast<const float4*>(src + sidx * split_stride + 4);
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  const uint32_t vecs_per_row = (uint32_t)d / 8;
+  const uint32_t total = (uint32_t)V * vecs_per_row;
+  const uint32_t i0 = (uint32_t)(blockIdx.x - first) * (kCopyThreads * kScatterVecs) + threadIdx.x;
+  const float* src[kScatterVecs];
+  bool live[kScatterVecs], have[kScatterVecs];
+#pragma unroll
+  for (int u = 0; u < kScatterVecs; ++u) {
+    const uint32_t i = i0 + u * kCopyThreads;
+    live[u] = i < total;
+    const uint32_t v = live[u] ? i / vecs_per_row : 0;
+    const uint32_t c8 = i - v * vecs_per_row;
+    const int p = !live[u] ? -1 : (vocab_pos ? vocab_pos[v] : (int)v);
+    have[u] = p >= 0;
+    src[u] = part + (int64_t)(have[u] ? p : 0) * d + c8 * 8;
+  }
+  float4 lo[kScatterVecs], hi[kScatterVecs];
+#pragma unroll
+  for (int u = 0; u < kScatterVecs; ++u) {
+    lo[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    hi[u] = lo[u];
+  }
+  for (int sidx = 0; sidx < splits; ++sidx) {
+    float4 a[kScatterVecs], b[kScatterVecs];
+#pragma unroll
+    for (int u = 0; u < kScatterVecs; ++u) {
+      if (have[u]) {
+        a[u] = *reinterpret_cast<const float4*>(src[u] + sidx * split_stride);
+        b[u] = *reinterpret_cast<const float4*>(src[u] + sidx * split_stride + 4);
+      } else {
+        a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        b[u] = a[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScatterVecs; ++u) {
+      lo[u].x += a[u].x; lo[u].y += a[u].y; lo[u].z += a[u].z; lo[u].w += a[u].w;
+      hi[u].x += b[u].x; hi[u].y += b[u].y; hi[u].z += b[u].z; hi[u].w += b[u].w;
     }
   }
-  if (BF16) {
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    reinterpret_cast<uint4*>(dW)[i] = o;
-  } else {
-    float4* out = reinterpret_cast<float4*>(dW) + 2 * i;
-    out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+  for (int u = 0; u < kScatterVecs; ++u) {
+    if (!live[u]) continue;
+    const uint32_t i = i0 + u * kCopyThreads;
+    if (BF16) {
+      uint4 o;
+      o.x = pack_bf16x2(lo[u].x, lo[u].y);
+      o.y = pack_bf16x2(lo[u].z, lo[u].w);
+      o.z = pack_bf16x2(hi[u].x, hi[u].y);
+      o.w = pack_bf16x2(hi[u].z, hi[u].w);
+      reinterpret_cast<uint4*>(dW)[i] = o;
+    } else {
+      float4* out = reinterpret_cast<float4*>(dW) + 2 * (size_t)i;
+      out[0] = lo[u];
+      out[1] = hi[u];
+    }
   }
 }
 
@@ -97,7 +128,8 @@ hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stri
                                const int32_t* vocab_pos, int V, int d, bool bf16, void* dW,
                                const LossOut* fin, hipStream_t s) {
   const int64_t total = (int64_t)V * (d / 8);
-  const int blocks = (int)((total + kCopyThreads - 1) / kCopyThreads);
+  constexpr int per_block = kCopyThreads * kScatterVecs;
+  const int blocks = (int)((total + per_block - 1) / per_block);
   const LossOut f = fin ? *fin : LossOut{nullptr, 0, nullptr, nullptr, nullptr};
   const int grid = blocks + (fin ? 1 : 0);
   if (grid > 0) {

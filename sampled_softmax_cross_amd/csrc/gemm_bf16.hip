@@ -1,16 +1,18 @@
 // Multi-stage bf16 MFMA GEMM for gfx950 (the logits, dX and dW products of the step).
 //
 // Every operand tile travels global -> LDS by buffer_load ... lds (no VGPR staging,
-// no ds_write), through an NS-deep ring of LDS stages of 32 k each, so a tile is
-// requested NS-1 stage-times before the MFMAs need it and the load latency of a
-// busy memory system stays hidden behind the matrix cores.
+// no ds_write), through an NS-deep ring of LDS stages of SK k each (32 or 64), so a
+// tile is requested NS-1 stage-times before the MFMAs need it and the load latency of
+// a busy memory system stays hidden behind the matrix cores.
 //
 // Operand layouts in LDS:
-//  * r-major (element (r, k) at P[r * ld + k], k contiguous): rows of 32 k = 64 B,
-//    the four 16-byte chunks of a row XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3;
-//    a fragment (8 consecutive k of one row) is one ds_read_b128.
+//  * r-major (element (r, k) at P[r * ld + k], k contiguous): rows of SK k (64 or
+//    128 B), the 16-byte chunks of a row XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3
+//    (SK = 32) or (row >> 1) & 7 (SK = 64); a fragment (8 consecutive k of one row) is
+//    one ds_read_b128. With SK = 64 every row of a stage is one whole 128-byte line of
+//    the operand, which halves the cache requests per byte against SK = 32.
 //  * k-major (element (r, k) at P[k * ld + r]): the tile is kept as it is in memory,
-//    32 rows of k, each R elements wide, 16-byte chunks XOR-swizzled by 4 * (k & 3).
+//    SK rows of k, each R elements wide, 16-byte chunks XOR-swizzled by 4 * (k & 3).
 //    Fragments are read with ds_read_b64_tr_b16: within each 16-lane group, lane j
 //    receives element i from the address supplied by lane 4i + j/4 (at element
 //    offset j % 4), so lanes that point at rows k..k+3 and 4-column groups assemble
@@ -26,7 +28,6 @@
 namespace sce {
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-constexpr int kStageK = 32;  // k per LDS stage
 
 // s_waitcnt vmcnt(n) with expcnt and lgkmcnt at their maxima (gfx9 encoding).
 template <int N>
@@ -46,33 +47,41 @@ __device__ __forceinline__ void wait_after(int after) {
   }
 }
 
+// LDS chunk (16 B) holding chunk `ch` of r-major row `row` (SK / 8 chunks per row).
+template <int SK>
+__device__ __forceinline__ int rm_swizzle(int row) {
+  if constexpr (SK == 32) return ((row >> 1) ^ (row >> 3)) & 3;
+  else return (row >> 1) & 7;
+}
+template <int SK>
 __device__ __forceinline__ int rm_index(int row, int ch) {
-  return row * 4 + (ch ^ (((row >> 1) ^ (row >> 3)) & 3));
+  return row * (SK / 8) + (ch ^ rm_swizzle<SK>(row));
 }
 template <int R>
 __device__ __forceinline__ int km_index(int k, int ch) {
   return k * (R / 8) + (ch ^ ((k & 3) << 2));
 }
 
-// One operand tile of R rows (r-major) or R columns (k-major) per stage, filled by
-// NW waves.
-template <int R, bool KMAJ, int NW>
+// One operand tile of R rows (r-major) or R columns (k-major) by SK k per stage,
+// filled by NW waves (64 chunks of 16 B per instruction).
+template <int R, bool KMAJ, int NW, int SK>
 struct DmaTile {
-  static_assert(R % (16 * NW) == 0 && (!KMAJ || R % 128 == 0), "tile shape");
-  static constexpr int kN = R / (16 * NW);  // DMA instructions per wave per stage
+  static_assert((R * SK) % (512 * NW) == 0 && (!KMAJ || R % 128 == 0), "tile shape");
+  static constexpr int kN = R * SK / (512 * NW);  // DMA instructions per wave per stage
   int off[kN];  // byte offset of the lane's chunk from the tile origin
   int kk[kN];   // k of the lane's chunk (r-major) or row (k-major), for the k clip
   int rr[kN];   // row (r-major) or first column (k-major) of the lane's chunk
-  __device__ __forceinline__ void init(int64_t ld) {
+  int w;        // index of this wave among the NW that fill the tile
+  __device__ __forceinline__ void init(int64_t ld, int wave) {
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    w = wave;
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int q = 64 * (w * kN + i) + lane;  // linear LDS chunk this lane fills
       int r, k;
       if constexpr (!KMAJ) {
-        r = q >> 2;
-        k = ((q & 3) ^ (((r >> 1) ^ (r >> 3)) & 3)) * 8;
+        r = q / (SK / 8);
+        k = ((q % (SK / 8)) ^ rm_swizzle<SK>(r)) * 8;
       } else {
         k = q / (R / 8);
         r = ((q % (R / 8)) ^ ((k & 3) << 2)) * 8;
@@ -87,7 +96,6 @@ struct DmaTile {
   __device__ __forceinline__ void issue(const bf16_t* base, int64_t rows_valid, int64_t k_valid,
                                         uint4* tile) const {
     const rsrc_t rs = make_rsrc(base);
-    const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kN; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -98,11 +106,11 @@ struct DmaTile {
 
 // Fragment of 8 consecutive k (k-step ks of the stage) for tile row/column `r`
 // (this lane's own; r already includes lane % 32).
-template <int R, bool KMAJ>
+template <int R, bool KMAJ, int SK>
 __device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int r_blk, int ks,
                                               int lane) {
   if constexpr (!KMAJ) {
-    return __builtin_bit_cast(bf16x8_t, tile[rm_index(r_lane, 2 * ks + (lane >> 5))]);
+    return __builtin_bit_cast(bf16x8_t, tile[rm_index<SK>(r_lane, 2 * ks + (lane >> 5))]);
   } else {
     const int G = lane >> 4, a = lane & 15;
     const int c = r_blk + 16 * (G & 1) + 4 * (a & 3);  // column this lane points at
@@ -126,7 +134,8 @@ __device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int
 // NS-deep LDS ring without a break between units: the first stages of the next unit
 // are already in flight while the current unit finishes and stores its tile.
 // BM x BN tile per unit, WGM x WGN waves; OCC workgroups share a CU.
-template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
+          int SK>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ Cout, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t kps,
@@ -134,9 +143,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int STAGE = (BM + BN) * 4;  // uint4 per stage (64 B per row/column)
-  constexpr int LPS = (BM + BN) / (16 * NW);  // DMA instructions per wave per stage
-  static_assert(NS >= 3 && LPS * (NS - 1) < 64, "pipeline depth");
+  constexpr int STAGE = (BM + BN) * SK / 8;  // uint4 per stage
+  constexpr int A_OFF = BM * SK / 8;          // B tile offset in a stage (uint4)
+  constexpr int LPS = (BM + BN) * SK / (512 * NW);  // DMA instructions per wave per stage
+  constexpr int KS = SK / 16;                       // MFMA k-steps per stage
+  static_assert((SK == 32 || SK == 64) && NS >= 2 && LPS * (NS - 1) < 64, "pipeline shape");
   __shared__ uint4 lds[NS * STAGE];
 
   const int lane = threadIdx.x & 63;
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   const int G = gridDim.x;
   if ((int)blockIdx.x >= nunits) return;
   const int my_units = (nunits - 1 - (int)blockIdx.x) / G + 1;
-  const int nk = (int)(kps / kStageK);  // stages per unit (kps is a positive multiple)
+  const int nk = (int)(kps / SK);  // stages per unit (kps is a positive multiple)
 
   struct Unit {
     int64_t m0, n0, kb, ke;
@@ -166,21 +177,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     return c;
   };
 
-  DmaTile<BM, A_KM, NW> ta;
-  DmaTile<BN, B_KM, NW> tb;
-  ta.init(lda);
-  tb.init(ldb);
+  DmaTile<BM, A_KM, NW, SK> ta;
+  DmaTile<BN, B_KM, NW, SK> tb;
+  ta.init(lda, wid);
+  tb.init(ldb, wid);
   // Issue cursor: unit iu, stage is of that unit. Past the last unit, stages are
   // issued fully clipped (zeros, no memory traffic) so every wait count is constant.
   int iu = 0, is = 0;
   Unit ic = unit(0);
   auto issue_next = [&](int slot_idx) {
     uint4* slot = lds + slot_idx * STAGE;
-    const int64_t k0 = ic.kb + (int64_t)is * kStageK;
+    const int64_t k0 = ic.kb + (int64_t)is * SK;
     const bool live = iu < my_units;
     const int64_t kv = live ? ic.ke - k0 : 0;
     ta.issue(A_KM ? A + k0 * lda + ic.m0 : A + ic.m0 * lda + k0, M - ic.m0, kv, slot);
-    tb.issue(B_KM ? B + k0 * ldb + ic.n0 : B + ic.n0 * ldb + k0, N - ic.n0, kv, slot + BM * 4);
+    tb.issue(B_KM ? B + k0 * ldb + ic.n0 : B + ic.n0 * ldb + k0, N - ic.n0, kv, slot + A_OFF);
     if (++is == nk) {
       is = 0;
       ++iu;
@@ -196,10 +207,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     const uint4* slot = lds + (g % NS) * STAGE;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      fa[buf][i] = read_frag<BM, A_KM>(slot, arow + i * 32 + l32, arow + i * 32, ks, lane);
+      fa[buf][i] = read_frag<BM, A_KM, SK>(slot, arow + i * 32 + l32, arow + i * 32, ks, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      fb[buf][j] = read_frag<BN, B_KM>(slot + BM * 4, bcol + j * 32 + l32, bcol + j * 32, ks, lane);
+      fb[buf][j] =
+          read_frag<BN, B_KM, SK>(slot + A_OFF, bcol + j * 32 + l32, bcol + j * 32, ks, lane);
   };
   f32x16_t acc[TM][TN];
   auto mfma_step = [&](int buf) {
@@ -240,19 +252,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     for (int s = 0; s < nk; ++s, ++g) {
-      // k-step 0 of stage g, with the reads of its k-step 1 in its shadow.
-      read_frags(g, 1, 1);
-      mfma_step(0);
-      interleave();
-      // Stage g + 1 becomes visible; slot g % NS has no readers left (both of its
+#pragma unroll
+      for (int q = 0; q + 1 < KS; ++q) {
+        // k-step q of stage g, with the reads of its k-step q + 1 in its shadow.
+        read_frags(g, q + 1, (q + 1) & 1);
+        mfma_step(q & 1);
+        interleave();
+      }
+      // Stage g + 1 becomes visible; slot g % NS has no readers left (all of its
       // fragment sets are in registers), so it takes stage g + NS.
       vm_wait<LPS * (NS - 2)>();
       __syncthreads();
       issue_next(g % NS);
-      // k-step 1 of stage g, with the first reads of stage g + 1 in its shadow (after
-      // the last stage these read a slot that is never used: in bounds, ignored).
+      // Last k-step of stage g, with the first reads of stage g + 1 in its shadow
+      // (after the last stage these read a slot that is never used: in bounds, ignored).
       read_frags(g + 1, 0, 0);
-      mfma_step(1);
+      mfma_step((KS - 1) & 1);
       interleave();
     }
     store_acc<OUT, TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow + l32, cc.n0 + bcol, lane >> 5,
@@ -260,22 +275,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   }
 }
 
-#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC)                              \
-  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC>(              \
+#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK)                          \
+  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK>(          \
       const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
       int64_t, int64_t, int);
-SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 3, 1)
-SCE_GEMM16_INST(128, 256, 2, 2, false, true, kOutBF16, 3, 2)
-SCE_GEMM16_INST(128, 256, 2, 2, false, true, kOutF32Split, 3, 2)
-SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2)
+SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 3, 1, 32)
+SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32)
+SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32)
+SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32)
 #undef SCE_GEMM16_INST
 
-template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC>
+template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
+          int SK>
 static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   const int splits = a.splits > 0 ? a.splits : 1;
   int64_t kps = (a.K + splits - 1) / splits;
-  kps = (kps + kStageK - 1) / kStageK * kStageK;
-  if (kps == 0) kps = kStageK;
+  kps = (kps + SK - 1) / SK * SK;
+  if (kps == 0) kps = SK;
   const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
   if (gx == 0 || gy == 0) return hipGetLastError();
   const int64_t units = gx * gy * splits;
@@ -284,7 +300,7 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   // workgroup's units on one XCD), or one per unit when there are fewer.
   const int slots = cu_count() * OCC;
   const int grid = (int)(units < slots ? units : slots);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC>),
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK>),
                      dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, s, static_cast<const bf16_t*>(a.A), a.lda,
                      static_cast<const bf16_t*>(a.B), a.ldb, a.C, a.ldc, a.M, a.N, a.K, kps,
                      a.split_stride, splits);
@@ -293,9 +309,9 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
 
 // Tile configurations (measured on MI355X with random bf16 inputs at the workload
 // shapes): the logits product uses 256 x 256 tiles with 8 waves (2 x 4, 128 x 64 each,
-// two waves per SIMD) and one workgroup per CU; dX and dW use 128 x 256 tiles with 4
-// waves and two workgroups per CU (their epilogues and stalls interleave). Three LDS
-// stages each.
+// two waves per SIMD) and one workgroup per CU; dX and dW use 128 x 256 tiles with two
+// workgroups per CU (their epilogues and stalls interleave), dX with 8 waves (64 x 64
+// each) and dW with 4 (64 x 128 each). Three LDS stages each.
 constexpr int kTileM = 128, kTileN = 256, kOcc = 2;
 
 int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass) {
@@ -324,11 +340,12 @@ int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split
 
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {
-    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 3, 1>(a, s);
+    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 3, 1, 32>(a, s);
     case Gemm::DX:
-      return a.splits > 1 ? run16<kTileM, kTileN, 2, 2, false, true, kOutF32Split, 3, kOcc>(a, s)
-                          : run16<kTileM, kTileN, 2, 2, false, true, kOutBF16, 3, kOcc>(a, s);
-    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc>(a, s);
+      return a.splits > 1
+                 ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32>(a, s)
+                 : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32>(a, s);
+    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc, 32>(a, s);
   }
   return hipErrorInvalidValue;
 }

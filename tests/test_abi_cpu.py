@@ -59,6 +59,8 @@ def test_workspace_size_host_checks(lib):
     assert _ws(10, 8, 131073, 10, 0)[0] == 1                 # V too large for a candidate build
     assert _ws(10, 8, 1 << 20, 0, 0)[0] == 0                  # ... fine for the full softmax
     assert _ws(10, 8, (1 << 20) + 1, 0, 0)[0] == 1            # beyond the full-softmax limit
+    assert _ws(1 << 20, 1 << 14, 4096, 64, 1)[0] == 0         # T * d == 2^34 is the largest
+    assert _ws((1 << 20) + 1, 1 << 14, 4096, 64, 1)[0] == 1   # T * d beyond 2^34
     assert lib.sce_workspace_size(1, 8, 8, 1, 0, None) == 1   # null output pointer
 
 
