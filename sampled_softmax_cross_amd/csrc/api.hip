@@ -31,6 +31,7 @@ int64_t mod64(int64_t a, int64_t m) {
 // Byte offsets of every workspace piece.
 struct Plan {
   int64_t Peff = 0, ldz = 0;
+  int64_t ldwc = 0;   // row pitch of the gathered W_C (elements)
   int splits = 1;     // k-split of the dW product (fp32 partials reduced by the scatter)
   int dx_splits = 1;  // k-split of the dX product (fp32 partials reduced into dX)
   size_t counters = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
@@ -56,7 +57,10 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
   p.ppos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
   p.row_loss = take((size_t)(T > 0 ? T : 1) * sizeof(float));
   if (full) {
-    p.wc = take(P > 0 ? (size_t)P * d * es : 0);
+    // W_C rows are padded by 64 elements: with d * es a multiple of 512 bytes (d = 768
+    // bf16: 1536 B), the logits product measured 15% slower on unpadded rows.
+    p.ldwc = P > 0 ? d + 64 : d;
+    p.wc = take(P > 0 ? (size_t)P * p.ldwc * es : 0);
     p.z = take((size_t)T * p.ldz * es);
     if (dtype == SCE_BF16) {
       p.splits = gemm_bf16_splits(p.Peff, d, T, 8, false);
@@ -165,7 +169,7 @@ sce_status sce_build_candidates(const int64_t* targets, const int64_t* prefix_ta
   int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
                                    (int)mod64(offset, V), counters, candidates_out, vocab_pos,
-                                   target_pos_out, ppos, nullptr, 0, nullptr, hs);
+                                   target_pos_out, ppos, nullptr, 0, nullptr, 0, hs);
   if (e == hipSuccess && aux_out) e = launch_write_aux(counters, aux_out, hs);
   return hip_status(e);
 }
@@ -211,10 +215,10 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   marks.mark(SCE_STAGE_CANDIDATES);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
                                    (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
-                                   W, (int)(d * es), ws + p.wc, hs);
+                                   W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), hs);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
-    GemmArgs g{x, d, WC, d, Z, p.ldz, T, p.Peff, d, 1, 0};
+    GemmArgs g{x, d, WC, p.ldwc, Z, p.ldz, T, p.Peff, d, 1, 0};
     e = launch_gemm(Gemm::Logits, bf16, g, hs);
   }
   marks.mark(SCE_STAGE_CE);
@@ -224,10 +228,10 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   marks.mark(SCE_STAGE_DX);
   if (e == hipSuccess && T > 0) {
     if (p.dx_splits > 1) {
-      GemmArgs g{Z, p.ldz, WC, d, part, d, T, d, p.Peff, p.dx_splits, T * d};
+      GemmArgs g{Z, p.ldz, WC, p.ldwc, part, d, T, d, p.Peff, p.dx_splits, T * d};
       e = launch_gemm(Gemm::DX, bf16, g, hs);
     } else {
-      GemmArgs g{Z, p.ldz, WC, d, dX, d, T, d, p.Peff, 1, 0};
+      GemmArgs g{Z, p.ldz, WC, p.ldwc, dX, d, T, d, p.Peff, 1, 0};
       e = launch_gemm(Gemm::DX, bf16, g, hs);
     }
   }

@@ -197,9 +197,9 @@ __global__ __launch_bounds__(256) void k_remap_gather(
     const int32_t* __restrict__ vocab_pos, int32_t* __restrict__ target_pos,
     int32_t* __restrict__ prefix_pos, int32_t* __restrict__ counters, int remap_blocks,
     const uint4* __restrict__ W, const int32_t* __restrict__ C, int row_vecs,
-    uint4* __restrict__ WC) {
+    uint4* __restrict__ WC, int wc_vecs) {
   if ((int)blockIdx.x >= remap_blocks) {
-    gather_rows_block((int)blockIdx.x - remap_blocks, W, C, P, row_vecs, WC);
+    gather_rows_block((int)blockIdx.x - remap_blocks, W, C, P, row_vecs, WC, wc_vecs);
     return;
   }
   __shared__ int scratch[256 / kWave + 1];
@@ -236,7 +236,8 @@ __global__ void k_write_aux(const int32_t* __restrict__ counters, int64_t* __res
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
                              int stride, int off, int32_t* counters, int32_t* C,
                              int32_t* vocab_pos, int32_t* target_pos, int32_t* prefix_pos,
-                             const void* W, int row_bytes, void* WC, hipStream_t s) {
+                             const void* W, int row_bytes, void* WC, int wc_row_bytes,
+                             hipStream_t s) {
   const bool mark_lds = V <= kMaxBitmapClasses;
   const size_t lds = mark_lds ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
   hipLaunchKernelGGL(k_cand, dim3(1), dim3(kBuildThreads), lds, s, targets, prefix, T, V, P,
@@ -247,7 +248,7 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
     hipLaunchKernelGGL(k_remap_gather, dim3(remap_blocks + gather_blocks), dim3(256), 0, s,
                        targets, prefix, T, V, P, vocab_pos, target_pos, prefix_pos, counters,
                        remap_blocks, reinterpret_cast<const uint4*>(W), C, row_bytes / 16,
-                       reinterpret_cast<uint4*>(WC));
+                       reinterpret_cast<uint4*>(WC), wc_row_bytes / 16);
   return hipGetLastError();
 }
 

@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK>(          \
       const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
       int64_t, int64_t, int);
-SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 3, 1, 32)
+SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64)
 SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32)
 SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32)
 SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32)
@@ -309,9 +309,11 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
 
 // Tile configurations (measured on MI355X with random bf16 inputs at the workload
 // shapes): the logits product uses 256 x 256 tiles with 8 waves (2 x 4, 128 x 64 each,
-// two waves per SIMD) and one workgroup per CU; dX and dW use 128 x 256 tiles with two
-// workgroups per CU (their epilogues and stalls interleave), dX with 8 waves (64 x 64
-// each) and dW with 4 (64 x 128 each). Three LDS stages each.
+// two waves per SIMD), one workgroup per CU and two LDS stages of 64 k (both of its
+// operands are r-major, whose 32-k stages would fetch half cache lines); dX and dW use
+// 128 x 256 tiles with two workgroups per CU (their epilogues and barrier stalls
+// interleave) and three stages of 32 k, dX with 8 waves (64 x 64 each) and dW with 4
+// (64 x 128 each).
 constexpr int kTileM = 128, kTileN = 256, kOcc = 2;
 
 int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass) {
@@ -340,7 +342,7 @@ int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split
 
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {
-    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 3, 1, 32>(a, s);
+    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64>(a, s);
     case Gemm::DX:
       return a.splits > 1
                  ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32>(a, s)

@@ -15,11 +15,13 @@ constexpr int kMaxBitmapClasses = 131072;
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
                              int stride, int off, int32_t* counters, int32_t* C,
                              int32_t* vocab_pos, int32_t* target_pos, int32_t* prefix_pos,
-                             const void* W, int row_bytes, void* WC, hipStream_t s);
+                             const void* W, int row_bytes, void* WC, int wc_row_bytes,
+                             hipStream_t s);
 hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s);
 
 // Row gather, one block of 256 lanes per kGatherRows rows: 32 lanes per row, each
-// moving whole 16-byte vectors, every load of a lane issued before its stores.
+// moving whole 16-byte vectors, every load of a lane issued before its stores. Rows of
+// W are row_vecs vectors apart, rows of W_C wc_vecs (>= row_vecs) apart.
 constexpr int kGatherRows = 8;
 inline int gather_block_count(int P, int row_vecs) {
   (void)row_vecs;
@@ -27,12 +29,13 @@ inline int gather_block_count(int P, int row_vecs) {
 }
 __device__ __forceinline__ void gather_rows_block(int blk, const uint4* __restrict__ W,
                                                   const int32_t* __restrict__ C, int P,
-                                                  int row_vecs, uint4* __restrict__ WC) {
+                                                  int row_vecs, uint4* __restrict__ WC,
+                                                  int wc_vecs) {
   const int r = blk * kGatherRows + (int)(threadIdx.x >> 5);
   if (r >= P) return;
   const int l = threadIdx.x & 31;
   const uint4* src = W + (int64_t)C[r] * row_vecs;
-  uint4* dst = WC + (int64_t)r * row_vecs;
+  uint4* dst = WC + (int64_t)r * wc_vecs;
   for (int v0 = l; v0 < row_vecs; v0 += 32 * 4) {
     const bool k1 = v0 + 32 < row_vecs, k2 = v0 + 64 < row_vecs, k3 = v0 + 96 < row_vecs;
     uint4 b1 = make_uint4(0, 0, 0, 0), b2 = b1, b3 = b1;
