@@ -64,7 +64,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     p.z = take((size_t)T * p.ldz * es);
     if (dtype == SCE_BF16) {
       p.splits = gemm_bf16_splits(p.Peff, d, T, 8, false);
-      p.dx_splits = gemm_bf16_splits(T, d, p.Peff, 4, true);
+      p.dx_splits = gemm_bf16_dx_splits(T, d, p.Peff);
     } else {
       p.splits = gemm_dw_splits(p.Peff, d, T);
     }
@@ -237,8 +237,8 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   }
   marks.mark(SCE_STAGE_DX_REDUCE);
   if (e == hipSuccess && T > 0 && p.dx_splits > 1)
-    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, bf16, dX, nullptr,
-                            hs);
+    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, nullptr, (int)T, (int)T, (int)d,
+                            bf16, dX, nullptr, hs);
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess) {
     GemmArgs g{Z, p.ldz, x, d, part, d, p.Peff, d, T, p.splits, p.Peff * d};
@@ -248,8 +248,8 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   if (e == hipSuccess) {
     // The dense scatter is the last launch; its extra block also finishes the loss.
     const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
-    e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? vocab_pos : nullptr, (int)V,
-                            (int)d, bf16, dW, &fin, hs);
+    e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? vocab_pos : nullptr,
+                            P > 0 ? cand : nullptr, (int)p.Peff, (int)V, (int)d, bf16, dW, &fin, hs);
   }
   marks.mark(SCE_NUM_STAGES);
   return hip_status(e);

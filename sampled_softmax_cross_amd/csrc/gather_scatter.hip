@@ -51,36 +51,64 @@ __device__ void finish_loss(const LossOut& f) {
   }
 }
 
-// Each lane produces kScatterVecs vectors of 8 consecutive output elements, spaced a
-// block apart so that every load of a lane is issued before its first store. With a
-// LossOut, block 0 finishes the loss (alongside the copy) and the copy uses blocks 1...
-// Flat vector indexes fit 32 bits: V * d / 8 <= 2^31 by the library's size limits.
+// One launch, three roles by block index:
+//  * with a LossOut, block 0 finishes the loss;
+//  * zero blocks clear every dW row that is not a candidate (vocab_pos < 0): one
+//    lookup per vector, then stores only;
+//  * row blocks write the candidate rows: dW[C[p], :] = sum over splits of
+//    part[s, p, :], with C = identity when no map is given. Their loads depend on
+//    nothing, the candidate's class only addresses the store.
+// Each lane handles kScatterVecs vectors of 8 consecutive elements, a block apart,
+// every load issued before the first store. Flat vector indexes fit 32 bits: V * d / 8
+// and T * d / 8 are at most 2^31 by the library's size limits.
 constexpr int kScatterVecs = 4;
+constexpr int kPerBlock = kCopyThreads * kScatterVecs;
+
+template <bool BF16>
+__device__ __forceinline__ void store_vec(void* dW, size_t i, const float4& lo, const float4& hi) {
+  if (BF16) {
+    uint4 o;
+    o.x = pack_bf16x2(lo.x, lo.y);
+    o.y = pack_bf16x2(lo.z, lo.w);
+    o.z = pack_bf16x2(hi.x, hi.y);
+    o.w = pack_bf16x2(hi.z, hi.w);
+    reinterpret_cast<uint4*>(dW)[i] = o;
+  } else {
+    float4* out = reinterpret_cast<float4*>(dW) + 2 * i;
+    out[0] = lo;
+    out[1] = hi;
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
     const float* __restrict__ part, int splits, int64_t split_stride,
-    const int32_t* __restrict__ vocab_pos, int V, int d, void* __restrict__ dW, int copy_blocks,
-    LossOut fin) {
-  const int first = (int)gridDim.x - copy_blocks;  // 1 with a LossOut, else 0
-  if ((int)blockIdx.x < first) {
+    const int32_t* __restrict__ vocab_pos, const int32_t* __restrict__ C, int rows, int V, int d,
+    void* __restrict__ dW, int zero_blocks, int row_blocks, LossOut fin) {
+  const int first = (int)gridDim.x - zero_blocks - row_blocks;  // 1 with a LossOut, else 0
+  const int b = (int)blockIdx.x - first;
+  if (b < 0) {
     finish_loss(fin);
     return;
   }
-  const uint32_t vecs_per_row = (uint32_t)d / 8;
-  const uint32_t total = (uint32_t)V * vecs_per_row;
-  const uint32_t i0 = (uint32_t)(blockIdx.x - first) * (kCopyThreads * kScatterVecs) + threadIdx.x;
-  const float* src[kScatterVecs];
-  bool live[kScatterVecs], have[kScatterVecs];
+  const uint32_t vpr = (uint32_t)d / 8;
+  if (b < zero_blocks) {
+    const uint32_t total = (uint32_t)V * vpr;
+    const uint32_t i0 = (uint32_t)b * kPerBlock + threadIdx.x;
+    int pos[kScatterVecs];
 #pragma unroll
-  for (int u = 0; u < kScatterVecs; ++u) {
-    const uint32_t i = i0 + u * kCopyThreads;
-    live[u] = i < total;
-    const uint32_t v = live[u] ? i / vecs_per_row : 0;
-    const uint32_t c8 = i - v * vecs_per_row;
-    const int p = !live[u] ? -1 : (vocab_pos ? vocab_pos[v] : (int)v);
-    have[u] = p >= 0;
-    src[u] = part + (int64_t)(have[u] ? p : 0) * d + c8 * 8;
+    for (int u = 0; u < kScatterVecs; ++u) {
+      const uint32_t i = i0 + u * kCopyThreads;
+      pos[u] = i < total ? vocab_pos[i / vpr] : 0;
+    }
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kScatterVecs; ++u)
+      if (pos[u] < 0) store_vec<BF16>(dW, i0 + u * kCopyThreads, z, z);
+    return;
   }
+  const uint32_t total = (uint32_t)rows * vpr;
+  const uint32_t i0 = (uint32_t)(b - zero_blocks) * kPerBlock + threadIdx.x;
   float4 lo[kScatterVecs], hi[kScatterVecs];
 #pragma unroll
   for (int u = 0; u < kScatterVecs; ++u) {
@@ -88,57 +116,51 @@ __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
     hi[u] = lo[u];
   }
   for (int sidx = 0; sidx < splits; ++sidx) {
-    float4 a[kScatterVecs], b[kScatterVecs];
+    float4 a[kScatterVecs], c[kScatterVecs];
 #pragma unroll
     for (int u = 0; u < kScatterVecs; ++u) {
-      if (have[u]) {
-        a[u] = *reinterpret_cast<const float4*>(src[u] + sidx * split_stride);
-        b[u] = *reinterpret_cast<const float4*>(src[u] + sidx * split_stride + 4);
+      const uint32_t i = i0 + u * kCopyThreads;
+      const float* src = part + sidx * split_stride + (size_t)i * 8;
+      if (i < total) {
+        a[u] = *reinterpret_cast<const float4*>(src);
+        c[u] = *reinterpret_cast<const float4*>(src + 4);
       } else {
         a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        b[u] = a[u];
+        c[u] = a[u];
       }
     }
 #pragma unroll
     for (int u = 0; u < kScatterVecs; ++u) {
       lo[u].x += a[u].x; lo[u].y += a[u].y; lo[u].z += a[u].z; lo[u].w += a[u].w;
-      hi[u].x += b[u].x; hi[u].y += b[u].y; hi[u].z += b[u].z; hi[u].w += b[u].w;
+      hi[u].x += c[u].x; hi[u].y += c[u].y; hi[u].z += c[u].z; hi[u].w += c[u].w;
     }
   }
 #pragma unroll
   for (int u = 0; u < kScatterVecs; ++u) {
-    if (!live[u]) continue;
     const uint32_t i = i0 + u * kCopyThreads;
-    if (BF16) {
-      uint4 o;
-      o.x = pack_bf16x2(lo[u].x, lo[u].y);
-      o.y = pack_bf16x2(lo[u].z, lo[u].w);
-      o.z = pack_bf16x2(hi[u].x, hi[u].y);
-      o.w = pack_bf16x2(hi[u].z, hi[u].w);
-      reinterpret_cast<uint4*>(dW)[i] = o;
-    } else {
-      float4* out = reinterpret_cast<float4*>(dW) + 2 * (size_t)i;
-      out[0] = lo[u];
-      out[1] = hi[u];
-    }
+    if (i >= total) continue;
+    const uint32_t p = i / vpr, c8 = i - p * vpr;
+    const uint32_t row = C ? (uint32_t)C[p] : p;
+    store_vec<BF16>(dW, (size_t)row * vpr + c8, lo[u], hi[u]);
   }
 }
 
 hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stride,
-                               const int32_t* vocab_pos, int V, int d, bool bf16, void* dW,
-                               const LossOut* fin, hipStream_t s) {
-  const int64_t total = (int64_t)V * (d / 8);
-  constexpr int per_block = kCopyThreads * kScatterVecs;
-  const int blocks = (int)((total + per_block - 1) / per_block);
+                               const int32_t* vocab_pos, const int32_t* C, int rows, int V, int d,
+                               bool bf16, void* dW, const LossOut* fin, hipStream_t s) {
+  const int64_t vpr = d / 8;
+  const int zero_blocks = vocab_pos ? (int)(((int64_t)V * vpr + kPerBlock - 1) / kPerBlock) : 0;
+  const int row_blocks = (int)(((int64_t)rows * vpr + kPerBlock - 1) / kPerBlock);
   const LossOut f = fin ? *fin : LossOut{nullptr, 0, nullptr, nullptr, nullptr};
-  const int grid = blocks + (fin ? 1 : 0);
+  const int grid = zero_blocks + row_blocks + (fin ? 1 : 0);
   if (grid > 0) {
     if (bf16)
       hipLaunchKernelGGL(k_scatter_rows<true>, dim3(grid), dim3(kCopyThreads), 0, s, part, splits,
-                         split_stride, vocab_pos, V, d, dW, blocks, f);
+                         split_stride, vocab_pos, C, rows, V, d, dW, zero_blocks, row_blocks, f);
     else
       hipLaunchKernelGGL(k_scatter_rows<false>, dim3(grid), dim3(kCopyThreads), 0, s, part,
-                         splits, split_stride, vocab_pos, V, d, dW, blocks, f);
+                         splits, split_stride, vocab_pos, C, rows, V, d, dW, zero_blocks,
+                         row_blocks, f);
   }
   return hipGetLastError();
 }

@@ -12,7 +12,8 @@
 //    one ds_read_b128. With SK = 64 every row of a stage is one whole 128-byte line of
 //    the operand, which halves the cache requests per byte against SK = 32.
 //  * k-major (element (r, k) at P[k * ld + r]): the tile is kept as it is in memory,
-//    SK rows of k, each R elements wide, 16-byte chunks XOR-swizzled by 4 * (k & 3).
+//    SK rows of k, each R elements wide, 16-byte chunks XOR-swizzled by 4 * (k & 3)
+//    (R a multiple of 128) or 4 * ((k >> 1) & 1) (R = 192).
 //    Fragments are read with ds_read_b64_tr_b16: within each 16-lane group, lane j
 //    receives element i from the address supplied by lane 4i + j/4 (at element
 //    offset j % 4), so lanes that point at rows k..k+3 and 4-column groups assemble
@@ -57,16 +58,25 @@ template <int SK>
 __device__ __forceinline__ int rm_index(int row, int ch) {
   return row * (SK / 8) + (ch ^ rm_swizzle<SK>(row));
 }
+// k-major chunk swizzle: rows k..k+3 that one transposing read touches land on
+// distinct 64-byte bank groups. Rows of a multiple of 256 bytes (R % 128 == 0) start
+// on the same banks, so they shift by 4 * (k & 3) chunks; 384-byte rows (R = 192)
+// alternate between two bank offsets, so rows k and k + 2 shift by 4 chunks.
+template <int R>
+__device__ __forceinline__ int km_swizzle(int k) {
+  if constexpr (R % 128 == 0) return (k & 3) << 2;
+  else return ((k >> 1) & 1) << 2;
+}
 template <int R>
 __device__ __forceinline__ int km_index(int k, int ch) {
-  return k * (R / 8) + (ch ^ ((k & 3) << 2));
+  return k * (R / 8) + (ch ^ km_swizzle<R>(k));
 }
 
 // One operand tile of R rows (r-major) or R columns (k-major) by SK k per stage,
 // filled by NW waves (64 chunks of 16 B per instruction).
 template <int R, bool KMAJ, int NW, int SK>
 struct DmaTile {
-  static_assert((R * SK) % (512 * NW) == 0 && (!KMAJ || R % 128 == 0), "tile shape");
+  static_assert((R * SK) % (512 * NW) == 0 && (!KMAJ || R % 128 == 0 || R == 192), "tile shape");
   static constexpr int kN = R * SK / (512 * NW);  // DMA instructions per wave per stage
   int off[kN];  // byte offset of the lane's chunk from the tile origin
   int kk[kN];   // k of the lane's chunk (r-major) or row (k-major), for the k clip
@@ -84,7 +94,7 @@ struct DmaTile {
         k = ((q % (SK / 8)) ^ rm_swizzle<SK>(r)) * 8;
       } else {
         k = q / (R / 8);
-        r = ((q % (R / 8)) ^ ((k & 3) << 2)) * 8;
+        r = ((q % (R / 8)) ^ km_swizzle<R>(k)) * 8;
       }
       kk[i] = k;
       rr[i] = r;
@@ -280,6 +290,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
       const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
       int64_t, int64_t, int);
 SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64)
+SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64)
+SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64)
 SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32)
 SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32)
 SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32)
@@ -308,21 +320,28 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
 }
 
 // Tile configurations (measured on MI355X with random bf16 inputs at the workload
-// shapes): the logits product uses 256 x 256 tiles with 8 waves (2 x 4, 128 x 64 each,
-// two waves per SIMD), one workgroup per CU and two LDS stages of 64 k (both of its
-// operands are r-major, whose 32-k stages would fetch half cache lines); dX and dW use
-// 128 x 256 tiles with two workgroups per CU (their epilogues and barrier stalls
-// interleave) and three stages of 32 k, dX with 8 waves (64 x 64 each) and dW with 4
-// (64 x 128 each).
+// shapes):
+//  * logits: 256 x 256 tiles, 8 waves (2 x 4, 128 x 64 each, two per SIMD), one
+//    workgroup per CU, two LDS stages of 64 k (both operands are r-major, whose 32-k
+//    stages would fetch half cache lines);
+//  * dX, N a multiple of 192: 256 x 192 tiles, 8 waves (4 x 2, 64 x 96 each), one
+//    workgroup per CU, two stages of 64 k: N = 768 gives 4 column tiles, so M = 16384
+//    fills the 256 CUs exactly once;
+//  * dX otherwise, and dW: 128 x 256 tiles with two workgroups per CU (their epilogues
+//    and barrier stalls interleave), three stages of 32 k, dX with 8 waves (64 x 64
+//    each) and dW with 4 (64 x 128 each).
 constexpr int kTileM = 128, kTileN = 256, kOcc = 2;
+constexpr int kWideM = 256, kWideN = 192;
+static bool dx_wide(int64_t N) { return N % kWideN == 0; }
 
-int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass) {
-  // Smallest k-split whose units fill at least 85% of the workgroup slots of the
-  // rounds they occupy (wave quantisation), keeping at least 1024 k per split. When a
-  // split needs an extra reduction pass (dX), it is only taken once the unsplit
-  // product already fills a full round of slots.
-  const int64_t tiles = ((M + kTileM - 1) / kTileM) * ((N + kTileN - 1) / kTileN);
-  const int64_t slots = (int64_t)cu_count() * kOcc;
+// Smallest k-split whose units fill at least 85% of the workgroup slots of the rounds
+// they occupy (wave quantisation), keeping at least 1024 k per split. When a split
+// needs an extra reduction pass (dX), it is only taken once the unsplit product
+// already fills a full round of slots.
+static int splits_for(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass,
+                      int bm, int bn, int occ) {
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int64_t slots = (int64_t)cu_count() * occ;
   if (split_costs_pass && tiles < slots) return 1;
   int best = 1;
   double best_eff = 0.0;
@@ -340,10 +359,23 @@ int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split
   return best;
 }
 
+int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass) {
+  return splits_for(M, N, K, max_splits, split_costs_pass, kTileM, kTileN, kOcc);
+}
+
+int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K) {
+  return dx_wide(N) ? splits_for(M, N, K, 4, true, kWideM, kWideN, 1)
+                    : splits_for(M, N, K, 4, true, kTileM, kTileN, kOcc);
+}
+
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {
     case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64>(a, s);
     case Gemm::DX:
+      if (dx_wide(a.N))
+        return a.splits > 1
+                   ? run16<kWideM, kWideN, 4, 2, false, true, kOutF32Split, 2, 1, 64>(a, s)
+                   : run16<kWideM, kWideN, 4, 2, false, true, kOutBF16, 2, 1, 64>(a, s);
       return a.splits > 1
                  ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32>(a, s)
                  : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32>(a, s);

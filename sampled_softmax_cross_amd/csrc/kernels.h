@@ -49,10 +49,11 @@ __device__ __forceinline__ void gather_rows_block(int blk, const uint4* __restri
     if (k3) dst[v0 + 96] = b3;
   }
 }
-// dW[v, :] = sum over splits of part[s, pos(v), :] (fp32) in dtype, or 0 when pos(v) < 0;
-// pos = vocab_pos, or the identity when vocab_pos is null. When `loss` is given, the
-// launch also finishes the step's scalars: loss = sum(row_loss[0..T)) / N in a fixed
-// order (0 when N == 0) and, when aux is given, the counters.
+// dW[C[p], :] = sum over splits of part[s, p, :] (fp32) in dtype for p < rows, and,
+// when vocab_pos is given, dW[v, :] = 0 for every v < V with vocab_pos[v] < 0. C null:
+// the identity (rows = V). When `fin` is given, the launch also finishes the step's
+// scalars: loss = sum(row_loss[0..T)) / N in a fixed order (0 when N == 0) and, when
+// aux is given, the counters.
 struct LossOut {
   const float* row_loss;
   int T;
@@ -61,8 +62,8 @@ struct LossOut {
   int64_t* aux;
 };
 hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stride,
-                               const int32_t* vocab_pos, int V, int d, bool bf16, void* dW,
-                               const LossOut* fin, hipStream_t s);
+                               const int32_t* vocab_pos, const int32_t* C, int rows, int V, int d,
+                               bool bf16, void* dW, const LossOut* fin, hipStream_t s);
 
 // Row-wise cross-entropy forward/backward over Z [T, ldz] (P valid columns), in place.
 hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
@@ -87,6 +88,8 @@ struct GemmArgs {
 // k-split factor for a GEMM of this shape (1 = no split). bf16 products only; the
 // fp32 products use gemm_dw_splits for dW and never split dX.
 int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass);
+// k-split of the bf16 dX product, for the tile shape its launch uses.
+int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K);
 int gemm_dw_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Gemm kind, bool bf16, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s);

@@ -25,6 +25,7 @@ CASES = [
     (129, 8, 50, 50, "f32", True, 0.3, 3),              # d = 8, P = V
     (64, 768, 50304, 10240, "bf16", True, 0.0, 20011),  # full vocabulary and hidden size
     (2050, 96, 2500, 1601, "bf16", False, 0.0, 3),
+    (700, 384, 3000, 1111, "bf16", True, 0.05, 7),     # d % 192 == 0: the 256 x 192 dX tiles, ragged
 ]
 
 

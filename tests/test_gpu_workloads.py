@@ -92,3 +92,28 @@ def test_workload(name):
     if w.calls > 1:
         # a class is drawn as a negative at most as often as a window covered it
         assert (neg_hits <= win_hits).all()
+
+
+def test_dx_split_sampled():
+    """A shape whose dX product is split along k (260 tiles of 256 x 192 on the chip's
+    256 compute units, so four splits reduced in fp32): sampled rows of dX, their L_t
+    and loss terms against the oracle, the candidate set exactly."""
+    T, d, V, P, stride, off = 16640, 768, 12000, 4608, 7919, 123
+    print(f"dx split: T={T} d={d} V={V} P={P} bf16", flush=True)
+    x, W, y, p = synth.small_case(11, T, d, V, "bf16", prefix=True, ignore_frac=0.02)
+    out = binding.forward_backward(to_dev(x, "bf16"), to_dev(W, "bf16"), labels_dev(y), labels_dev(p),
+                                   P, stride, off, want_rows=True)
+    torch.cuda.synchronize()
+    cand = build_candidates(V, P, stride, off, y, p)
+    assert np.array_equal(out["C"].cpu().numpy(), cand["C"])
+    xf, Wf = inputs_f64(x, W, "bf16")
+    WC = Wf[cand["C"]]
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 255, 256, T - 257, T - 1], rng.integers(0, T, 27)]))
+    L = np.zeros(T)
+    L[rows] = ce.lse_rows(xf, WC, rows)
+    tol = TOL["bf16"]
+    np.testing.assert_allclose(to_f64(out["row_lse"])[rows], L[rows], rtol=tol["loss"], atol=0)
+    ref = ce.dx_rows(xf, WC, L, cand["target_pos"], cand["prefix_pos"], cand["N"], rows)
+    got = to_f64(out["dX"][torch.from_numpy(rows).cuda()])
+    assert max_rel(got, ref) <= tol["grad"], max_rel(got, ref)
