@@ -91,9 +91,9 @@ def main():
                          "for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sampled-CE "
-              "step has no cross-GPU exchange inside it, see the sharding notes in DESIGN.md",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the sampled-CE "
+              "step has no cross-GPU exchange inside it, so one GPU's share of a data-parallel "
+              "batch is the unit measured here", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -66,7 +66,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
       p.splits = gemm_bf16_splits(p.Peff, d, T, 8, false);
       p.dx_splits = gemm_bf16_dx_splits(T, d, p.Peff);
     } else {
-      p.splits = gemm_dw_splits(p.Peff, d, T);
+      p.splits = gemm_f32_splits(p.Peff, d, T);
+      p.dx_splits = gemm_f32_splits(T, d, p.Peff);
     }
     // One region serves both products' partials (dX's are reduced before dW runs).
     const size_t dw_part = (size_t)p.splits * p.Peff * d;

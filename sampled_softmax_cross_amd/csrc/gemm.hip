@@ -271,11 +271,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
                         OUT == kOutF32Split ? (int64_t)blockIdx.y * split_stride : 0);
 }
 
-int gemm_dw_splits(int64_t M, int64_t N, int64_t K) {
-  // Tiles of the bf16 dW product; split k until the grid fills the chip.
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+int gemm_f32_splits(int64_t M, int64_t N, int64_t K) {
+  // 128 x 128 tiles of the fp32 products: double the k-split while the units still
+  // fit one round of workgroups on 256 CUs and every split keeps at least 256 k.
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int s = 1;
-  while (s < 8 && tiles * s < 256 && K / (2 * s) >= 2048) s *= 2;
+  while (s < 64 && tiles * s * 2 <= 256 && K / (2 * s) >= 256) s *= 2;
   return s;
 }
 
@@ -287,6 +288,7 @@ int gemm_dw_splits(int64_t M, int64_t N, int64_t K) {
                                                           int64_t, int64_t, int64_t, int64_t);
 SCE_GEMM_INST(float, 128, 128, true, true, kOutF32)
 SCE_GEMM_INST(float, 128, 128, true, false, kOutF32)
+SCE_GEMM_INST(float, 128, 128, true, false, kOutF32Split)
 SCE_GEMM_INST(float, 128, 128, false, false, kOutF32Split)
 #undef SCE_GEMM_INST
 
@@ -311,7 +313,9 @@ hipError_t launch_gemm(Gemm kind, bool bf16, const GemmArgs& a, hipStream_t s) {
   if (bf16) return launch_gemm_bf16(kind, a, s);
   switch (kind) {
     case Gemm::Logits: return run<float, 128, 128, true, true, kOutF32>(a, s);
-    case Gemm::DX: return run<float, 128, 128, true, false, kOutF32>(a, s);
+    case Gemm::DX:
+      return a.splits > 1 ? run<float, 128, 128, true, false, kOutF32Split>(a, s)
+                          : run<float, 128, 128, true, false, kOutF32>(a, s);
     case Gemm::DW: return run<float, 128, 128, false, false, kOutF32Split>(a, s);
   }
   return hipErrorInvalidValue;

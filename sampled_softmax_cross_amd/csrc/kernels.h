@@ -85,12 +85,12 @@ struct GemmArgs {
   int splits;            // split-K factor (DW only)
   int64_t split_stride;  // elements between split slabs of C (DW only)
 };
-// k-split factor for a GEMM of this shape (1 = no split). bf16 products only; the
-// fp32 products use gemm_dw_splits for dW and never split dX.
+// k-split factor for a GEMM of this shape (1 = no split). bf16 products; the fp32
+// products use gemm_f32_splits.
 int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass);
 // k-split of the bf16 dX product, for the tile shape its launch uses.
 int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K);
-int gemm_dw_splits(int64_t M, int64_t N, int64_t K);
+int gemm_f32_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Gemm kind, bool bf16, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s);
 
