@@ -65,6 +65,7 @@ def test_workload(name):
             loss, row_loss, N2 = ce.loss_from_lse(xf, WC, L, tpos, ppos)
             assert N2 == N
             got = float(out["loss"].item())
+            print(f"  loss {got:.7f} oracle {loss:.7f} rel {abs(got - loss) / abs(loss):.2e}", flush=True)
             assert abs(got - loss) <= tol["loss"] * abs(loss), (got, loss)
             np.testing.assert_allclose(gl, L, rtol=tol["loss"], atol=0)
             assert max_rel(to_f64(out["row_loss"]), row_loss) <= 10 * tol["loss"]
@@ -75,6 +76,7 @@ def test_workload(name):
             ref = ce.dwc_rows(xf, WC, L, tpos, ppos, N, js)
             cls = js if w.P == 0 else cand["C"][js]
             gW_rows = to_f64(out["dW"][torch.from_numpy(cls).cuda()])
+            print(f"  dW rows max-rel {max_rel(gW_rows, ref):.2e}", flush=True)
             assert max_rel(gW_rows, ref) <= tol["grad"], max_rel(gW_rows, ref)
             L_rows = L
         else:
@@ -82,6 +84,7 @@ def test_workload(name):
             np.testing.assert_allclose(gl[rows], L_rows[rows], rtol=tol["loss"], atol=0)
         ref = ce.dx_rows(xf, WC, L_rows, tpos, ppos, N, rows)
         gX_rows = to_f64(out["dX"][torch.from_numpy(rows).cuda()])
+        print(f"  dX rows max-rel {max_rel(gX_rows, ref):.2e}", flush=True)
         assert max_rel(gX_rows, ref) <= tol["grad"], max_rel(gX_rows, ref)
         if w.P > 0:
             outside = np.setdiff1d(np.arange(w.V), cand["C"])
