@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--micro", choices=["softmax", "gather"], default=None,
+                    help="instead of the step: time one building block on its own over the "
+                         "secondary workloads (one JSON line per shape)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (a known-size reference "
                          "for HBM traffic counters)")
@@ -101,6 +104,9 @@ def main():
 
     from sampled_softmax_cross_amd import binding, synth
 
+    if args.micro:
+        micro(args.micro)
+        return
     w = synth.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -225,6 +231,83 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def _time_ms(fn, reps=50, warmup=10):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def micro(kind):
+    """Building blocks over the pages' secondary workloads.
+
+    softmax: the fused row CE forward/backward (read a row, write its gradient) over
+    M = 4096 rows and N = 256 .. 12672 columns ("Learning Triton one kernel at a time:
+    softmax", its benchmark sweep; bandwidth counted as 2 * M * N * element bytes),
+    fp32 and bf16, next to PyTorch's softmax forward on the same tensor.
+    gather: the row gather (index select) of bf16 rows of 4096 for the index counts of
+    torchtitan PR #1083's benchmark script ([1024, 512], [4096, 4096], [8192, 8192]
+    rows and indices), bandwidth as read + write, next to torch.index_select.
+    """
+    import numpy as np
+    import torch
+
+    from sampled_softmax_cross_amd import binding
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    import ctypes
+    lib = binding.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P_ = ctypes.c_void_p
+    if kind == "softmax":
+        M = 4096
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        nbytes = ctypes.c_size_t(0)
+        lib.sce_ce_rows_workspace_size(M, ctypes.byref(nbytes))
+        ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+        for dt, es in ((torch.float32, 4), (torch.bfloat16, 2)):
+            for N in (256, 512, 1024, 2048, 3072, 4096, 6144, 8192, 10240, 12672):
+                Z = torch.randn(M, N, generator=gen, device=dev).to(dt)
+                tp = torch.randint(0, N, (M,), generator=gen, device=dev, dtype=torch.int32)
+                Zs = Z.clone()
+                # the C entry point with its arguments prepared once (no Python work per call)
+                args = (P_(Z.data_ptr()), N, M, N, binding.dtype_code(dt), P_(tp.data_ptr()), None,
+                        P_(loss.data_ptr()), None, None, None, P_(ws.data_ptr()), ws.numel(), stream)
+                ms = _time_ms(lambda: lib.sce_ce_rows(*args))
+                ms_t = _time_ms(lambda: torch.softmax(Zs, dim=1))
+                gbs = 2.0 * M * N * es / (ms * 1e-3) / 1e9
+                print(json.dumps({"micro": "softmax_ce_rows", "M": M, "N": N,
+                                  "dtype": "bf16" if es == 2 else "f32", "us": round(ms * 1e3, 2),
+                                  "GB/s": round(gbs, 1), "frac_hbm": round(gbs / 8000.0, 4),
+                                  "torch_softmax_us": round(ms_t * 1e3, 2)}), flush=True)
+    else:
+        d = 4096
+        for rows, n in ((1024, 512), (4096, 4096), (8192, 8192)):
+            W = torch.randn(rows, d, generator=gen, device=dev).to(torch.bfloat16)
+            idx = torch.randint(0, rows, (n,), generator=gen, device=dev, dtype=torch.int32)
+            out = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+            idx64 = idx.long()
+            args = (P_(W.data_ptr()), rows, d, P_(idx.data_ptr()), n, binding.SCE_BF16,
+                    P_(out.data_ptr()), d, None, stream)
+            ms = _time_ms(lambda: lib.sce_gather_rows(*args))
+            ms_t = _time_ms(lambda: torch.index_select(W, 0, idx64, out=out))
+            byts = 2.0 * n * d * 2
+            print(json.dumps({"micro": "gather_rows", "rows": rows, "d": d, "indices": n,
+                              "dtype": "bf16", "us": round(ms * 1e3, 2),
+                              "TB/s": round(byts / (ms * 1e-3) / 1e12, 3),
+                              "frac_hbm": round(byts / (ms * 1e-3) / 8e12, 4),
+                              "torch_index_select_us": round(ms_t * 1e3, 2)}), flush=True)
 
 
 def cpu_baseline(w, x, W, y, p, sample_tokens):

@@ -144,6 +144,47 @@ SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, con
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * sce_ce_rows -- the fused cross-entropy forward/backward of the step on its own, in
+ * place over a caller's logits ("Learning Triton one kernel at a time: softmax":
+ * row maximum, online (max, sum) merge, softmax gradient; "sampled_softmax.py"
+ * docstring and "16_optimization_checks.py" lm_gradient for the labels and N):
+ *   for each row t of Z [T, ldz] with columns [0, P) valid,
+ *     L_t        = max_j Z_tj + ln sum_j exp(Z_tj - max_j Z_tj)
+ *     row loss_t = [y_t >= 0] (L_t - Z_t,y_t) + [p_t >= 0] (L_t - Z_t,p_t)
+ *     Z_tj      <- (n_t exp(Z_tj - L_t) - [j = y_t] - [j = p_t]) / N
+ *   with y_t = target_pos[t], p_t = prefix_pos[t], n_t = [y_t >= 0] + [p_t >= 0],
+ *   N = sum_t n_t (counted on the device) and loss = sum_t row loss_t / N (0 when N = 0).
+ *
+ *   Z           [T, ldz] dtype, P <= ldz, ldz % 8 == 0, 16-byte aligned; overwritten
+ *               (columns [P, ldz) receive zeros).
+ *   target_pos  [T] int32 in [-1, P).    prefix_pos [T] int32 or NULL (= all -1).
+ *   loss [1] float32.  row_loss_out, row_lse_out [T] float32 or NULL.
+ *   aux_out [4] int64 or NULL: {0, N, 0, SCE_DEV_* bits}. A position outside [-1, P)
+ *   sets SCE_DEV_LABEL_RANGE and is treated as -1.
+ *   workspace  at least sce_ce_rows_workspace_size(T) bytes, 256-byte aligned.
+ */
+SCE_API sce_status sce_ce_rows_workspace_size(int64_t T, size_t* bytes);
+SCE_API sce_status sce_ce_rows(void* Z, int64_t ldz, int64_t T, int64_t P, int dtype,
+                               const int32_t* target_pos, const int32_t* prefix_pos, float* loss,
+                               float* row_loss_out, float* row_lse_out, int64_t* aux_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sce_gather_rows -- the row gather of the step on its own ("sampled_softmax.py",
+ * SampledSoftmax._gather_rows): out[i, 0:d] = W[idx[i], 0:d] for i < n, bit for bit.
+ *   W [V, d] dtype row-major, 16-byte aligned, d % 8 == 0.
+ *   idx [n] int32. An index outside [0, V) gives a row of zeros and, when status_out
+ *   is not NULL, ORs SCE_DEV_LABEL_RANGE into *status_out (a device int32 the caller
+ *   clears beforehand).
+ *   out [n, ld_out] dtype, ld_out >= d, ld_out % 8 == 0, 16-byte aligned; columns
+ *   [d, ld_out) are not written.
+ * No workspace; enqueued on `stream`.
+ */
+SCE_API sce_status sce_gather_rows(const void* W, int64_t V, int64_t d, const int32_t* idx,
+                                   int64_t n, int dtype, void* out, int64_t ld_out,
+                                   int32_t* status_out, void* stream);
+
+/*
  * Stage timing for benchmarks. sce_profile_enable(1) makes every later call of
  * sampled_ce_forward_backward record a HIP event on its stream at each stage
  * boundary (up to 512 calls; later calls are not timed); sce_profile_enable(0)

@@ -52,25 +52,17 @@ def logsumexp_rows(z):
     return m[:, 0] + np.log(np.exp(z - m).sum(axis=1))
 
 
-def forward_backward(x, W, C, target_pos, prefix_pos=None):
-    """Dense oracle: returns (loss, dX [T,d], dW [V,d], L [T], row_loss [T]).
-
-    x [T,d] and W [V,d] are float64 (exact widenings of the inputs); C is the
-    int array of candidate classes (None for the full softmax).
-    """
-    x = np.asarray(x, dtype=np.float64)
-    W = np.asarray(W, dtype=np.float64)
-    T, d = x.shape
-    V = W.shape[0]
-    WC = _wc(W, C)
-    P = WC.shape[0]
+def ce_rows(z, target_pos, prefix_pos=None):
+    """The cross-entropy part of the definition from the logits z [T, P] (float64):
+    returns (loss, g [T, P], L [T], row_loss [T], N)."""
+    z = np.asarray(z, dtype=np.float64)
+    T, P = z.shape
     tpos = np.asarray(target_pos, dtype=np.int64)
     ppos = None if prefix_pos is None else np.asarray(prefix_pos, dtype=np.int64)
     n = _label_counts(tpos, ppos)
     N = int(n.sum())
     if T == 0:
-        return 0.0, np.zeros((0, d)), np.zeros((V, d)), np.zeros(0), np.zeros(0)
-    z = x @ WC.T
+        return 0.0, np.zeros((0, P)), np.zeros(0), np.zeros(0), N
     L = logsumexp_rows(z)
     rows = np.arange(T)
     row_loss = np.zeros(T)
@@ -83,9 +75,25 @@ def forward_backward(x, W, C, target_pos, prefix_pos=None):
         row_loss[has_p] += L[has_p] - z[rows[has_p], ppos[has_p]]
         np.add.at(onehot, (rows[has_p], ppos[has_p]), 1.0)
     if N == 0:
-        return 0.0, np.zeros((T, d)), np.zeros((V, d)), L, row_loss
-    loss = row_loss.sum() / N
+        return 0.0, np.zeros((T, P)), L, row_loss, N
     g = (n[:, None] * np.exp(z - L[:, None]) - onehot) / N
+    return float(row_loss.sum() / N), g, L, row_loss, N
+
+
+def forward_backward(x, W, C, target_pos, prefix_pos=None):
+    """Dense oracle: returns (loss, dX [T,d], dW [V,d], L [T], row_loss [T]).
+
+    x [T,d] and W [V,d] are float64 (exact widenings of the inputs); C is the
+    int array of candidate classes (None for the full softmax).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    T, d = x.shape
+    V = W.shape[0]
+    WC = _wc(W, C)
+    if T == 0:
+        return 0.0, np.zeros((0, d)), np.zeros((V, d)), np.zeros(0), np.zeros(0)
+    loss, g, L, row_loss, N = ce_rows(x @ WC.T, target_pos, prefix_pos)
     dX = g @ WC
     dWC = g.T @ x
     dW = np.zeros((V, d))
@@ -93,7 +101,7 @@ def forward_backward(x, W, C, target_pos, prefix_pos=None):
         dW[:] = dWC
     else:
         dW[np.asarray(C, dtype=np.int64)] = dWC
-    return float(loss), dX, dW, L, row_loss
+    return loss, dX, dW, L, row_loss
 
 
 # ---------------------------------------------------------------------------

@@ -18,6 +18,7 @@ DEV_TOO_MANY_TARGETS, DEV_LABEL_RANGE = 1, 2
 STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
 
 EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sampled_ce_forward_backward",
+           "sce_ce_rows_workspace_size", "sce_ce_rows", "sce_gather_rows",
            "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
 STAGES = ("candidates", "logits", "ce", "dx", "dx_reduce", "dw", "scatter")
 
@@ -48,6 +49,12 @@ def load_library(path: str = LIB_PATH):
     lib.sampled_ce_forward_backward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                                 p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.sampled_ce_forward_backward.restype = i32
+    lib.sce_ce_rows_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
+    lib.sce_ce_rows_workspace_size.restype = i32
+    lib.sce_ce_rows.argtypes = [p, i64, i64, i64, i32, p, p, p, p, p, p, p, sz, p]
+    lib.sce_ce_rows.restype = i32
+    lib.sce_gather_rows.argtypes = [p, i64, i64, p, i64, i32, p, i64, p, p]
+    lib.sce_gather_rows.restype = i32
     lib.sce_status_string.argtypes = [i32]
     lib.sce_status_string.restype = ctypes.c_char_p
     lib.sce_profile_enable.argtypes = [i32]
@@ -178,6 +185,61 @@ def forward_backward(x, W, targets, prefix_targets, P, stride, offset, *, output
     o["target_pos"] = o["target_pos"][:T]
     o["prefix_pos"] = o["prefix_pos"][:T]
     return o
+
+
+def ce_rows(Z, P, target_pos, prefix_pos=None, *, want_rows=False, ws=None):
+    """The fused CE forward/backward alone, in place: Z [T, ldz] (bf16 or fp32,
+    contiguous, ldz % 8 == 0) holds logits in columns [0, P) and is overwritten with
+    their gradient. target_pos / prefix_pos are int32 [T] positions in [0, P) or -1.
+    Returns dict: loss (fp32 [1]), aux (int64 [4]: 0, N, 0, device status) and with
+    want_rows row_lse, row_loss (fp32 [T])."""
+    lib = load_library()
+    dev = Z.device
+    T, ldz = Z.shape
+    if not Z.is_contiguous():
+        raise ValueError("Z must be contiguous")
+    for t in (target_pos, prefix_pos):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.shape[0] != T):
+            raise ValueError("label positions must be contiguous int32 [T]")
+    o = {"loss": torch.empty(1, dtype=torch.float32, device=dev),
+         "aux": torch.empty(4, dtype=torch.int64, device=dev)}
+    if want_rows:
+        o["row_lse"] = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+        o["row_loss"] = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+    out = ctypes.c_size_t(0)
+    rc = lib.sce_ce_rows_workspace_size(T, ctypes.byref(out))
+    if rc != 0:
+        raise SceError("sce_ce_rows_workspace_size", rc)
+    if ws is None:
+        ws = workspace(out.value, dev)
+    rc = lib.sce_ce_rows(_ptr(Z), ldz, T, P, dtype_code(Z.dtype), _ptr(target_pos),
+                         _ptr(prefix_pos), _ptr(o["loss"]), _ptr(o.get("row_loss")),
+                         _ptr(o.get("row_lse")), _ptr(o["aux"]), _ptr(ws), ws.numel(), _stream(dev))
+    if rc != 0:
+        raise SceError("sce_ce_rows", rc)
+    return o
+
+
+def gather_rows(W, idx, *, out=None, status=None):
+    """out[i] = W[idx[i]] (bit for bit) for W [V, d] (bf16 or fp32, contiguous) and
+    int32 idx [n]; rows of out may be padded (out [n, ld_out], ld_out % 8 == 0). An
+    index outside [0, V) gives zeros and, with a zeroed int32 [1] `status`, sets
+    DEV_LABEL_RANGE in it."""
+    lib = load_library()
+    dev = W.device
+    V, d = W.shape
+    n = idx.shape[0]
+    if not W.is_contiguous() or idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("W must be contiguous and idx contiguous int32")
+    if out is None:
+        out = torch.empty(n, d, dtype=W.dtype, device=dev)
+    if out.dtype != W.dtype or out.shape[0] != n or out.stride(1) != 1 or out.shape[1] < d:
+        raise ValueError("out must be [n, >= d] with unit column stride, dtype of W")
+    rc = lib.sce_gather_rows(_ptr(W), V, d, _ptr(idx), n, dtype_code(W.dtype), _ptr(out),
+                             out.stride(0), _ptr(status), _stream(dev))
+    if rc != 0:
+        raise SceError("sce_gather_rows", rc)
+    return out
 
 
 def profile_enable(on: bool) -> None:

@@ -256,6 +256,81 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   return hip_status(e);
 }
 
+// ---- building blocks on their own ---------------------------------------------
+
+namespace {
+struct CePlan {
+  size_t counters = 0, tpos = 0, ppos = 0, row_loss = 0, total = 0;
+};
+CePlan make_ce_plan(int64_t T) {
+  CePlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t n = (size_t)(T > 0 ? T : 1);
+  p.counters = take(kNumCounters * sizeof(int32_t));
+  p.tpos = take(n * sizeof(int32_t));
+  p.ppos = take(n * sizeof(int32_t));
+  p.row_loss = take(n * sizeof(float));
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+sce_status sce_ce_rows_workspace_size(int64_t T, size_t* bytes) {
+  if (bytes == nullptr || T < 0 || T > INT32_MAX / 2) return SCE_EINVAL;
+  *bytes = make_ce_plan(T).total;
+  return SCE_OK;
+}
+
+sce_status sce_ce_rows(void* Z, int64_t ldz, int64_t T, int64_t P, int dtype,
+                       const int32_t* target_pos, const int32_t* prefix_pos, float* loss,
+                       float* row_loss_out, float* row_lse_out, int64_t* aux_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (T < 0 || T > INT32_MAX / 2 || P < 1 || P > SCE_MAX_V) return SCE_EINVAL;
+  if (ldz < P || ldz % 8 != 0 || ldz > (int64_t)SCE_MAX_V + 8) return SCE_EINVAL;
+  if (dtype != SCE_F32 && dtype != SCE_BF16) return SCE_EINVAL;
+  if (loss == nullptr || (T > 0 && (Z == nullptr || target_pos == nullptr))) return SCE_EINVAL;
+  if (Z && !aligned16(Z)) return SCE_EINVAL;
+  const CePlan p = make_ce_plan(T);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  int32_t* tpos = reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+  const bool bf16 = dtype == SCE_BF16;
+  hipError_t e = launch_ce_prep(target_pos, prefix_pos, (int)T, (int)P, tpos, ppos, counters, hs);
+  if (e == hipSuccess)
+    e = launch_ce_rows(Z, ldz, (int)T, (int)P, bf16, tpos, ppos, counters, row_loss, row_lse_out,
+                       hs);
+  if (e == hipSuccess) {
+    // the scatter launch with no rows: only its loss block runs
+    const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
+    e = launch_scatter_rows(nullptr, 0, 0, nullptr, nullptr, 0, 0, 8, bf16, nullptr, &fin, hs);
+  }
+  return hip_status(e);
+}
+
+sce_status sce_gather_rows(const void* W, int64_t V, int64_t d, const int32_t* idx, int64_t n,
+                           int dtype, void* out, int64_t ld_out, int32_t* status_out,
+                           void* stream) {
+  if (V < 1 || n < 0 || n > INT32_MAX / 2 || d < 8 || d % 8 != 0 || d > SCE_MAX_D) return SCE_EINVAL;
+  if (dtype != SCE_F32 && dtype != SCE_BF16) return SCE_EINVAL;
+  if (ld_out < d || ld_out % 8 != 0) return SCE_EINVAL;
+  if (n > 0 && (W == nullptr || idx == nullptr || out == nullptr)) return SCE_EINVAL;
+  if ((W && !aligned16(W)) || (out && !aligned16(out))) return SCE_EINVAL;
+  if (n == 0) return SCE_OK;
+  const int64_t es = dtype == SCE_BF16 ? 2 : 4;
+  return hip_status(launch_gather_checked(W, V, idx, (int)n, (int)(d * es), out, ld_out * es,
+                                          status_out, static_cast<hipStream_t>(stream)));
+}
+
 sce_status sce_profile_enable(int on) {
   if (on && !g_prof.on) g_prof.calls = 0;  // a new timing window; disabling keeps the record
   g_prof.on = on != 0;

@@ -350,6 +350,48 @@ static void launch_ce_typed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
   }
 }
 
+// Label positions given by a caller (the CE alone): one workgroup copies them with
+// every position outside [-1, P) replaced by -1 (flagged), counts N and sets the
+// counters the CE kernel and the loss reduction read.
+__global__ __launch_bounds__(1024) void k_ce_prep(const int32_t* __restrict__ tpos_in,
+                                                  const int32_t* __restrict__ ppos_in, int T,
+                                                  int P, int32_t* __restrict__ tpos,
+                                                  int32_t* __restrict__ ppos,
+                                                  int32_t* __restrict__ counters) {
+  __shared__ int scratch[1024 / kWave + 1];
+  int n = 0, bad = 0;
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+    int a = tpos_in[t];
+    if (a < -1 || a >= P) {
+      bad = 1;
+      a = -1;
+    }
+    tpos[t] = a;
+    n += a >= 0;
+    int b = ppos_in ? ppos_in[t] : -1;
+    if (b < -1 || b >= P) {
+      bad = 1;
+      b = -1;
+    }
+    ppos[t] = b;
+    n += b >= 0;
+  }
+  const int N = block_sum_int(n, scratch);
+  const int any_bad = block_sum_int(bad, scratch);
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < kNumCounters; ++i) counters[i] = 0;
+    counters[kNumLabels] = N;
+    counters[kStatus] = any_bad ? kDevLabelRange : 0;
+  }
+}
+
+hipError_t launch_ce_prep(const int32_t* tpos_in, const int32_t* ppos_in, int T, int P,
+                          int32_t* tpos, int32_t* ppos, int32_t* counters, hipStream_t s) {
+  hipLaunchKernelGGL(k_ce_prep, dim3(1), dim3(1024), 0, s, tpos_in, ppos_in, T, P, tpos, ppos,
+                     counters);
+  return hipGetLastError();
+}
+
 hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
                           const int32_t* target_pos, const int32_t* prefix_pos,
                           const int32_t* counters, float* row_loss, float* row_lse,

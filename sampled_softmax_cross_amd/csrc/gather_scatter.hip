@@ -1,5 +1,5 @@
-// The dense scatter of the candidate-row gradient (the row gather lives in
-// kernels.h and runs inside the remap launch).
+// The dense scatter of the candidate-row gradient, and the row gather on its own (the
+// step's gather lives in kernels.h and runs inside the remap launch).
 //
 // Both are pure data movement ("sampled_softmax.py", SampledSoftmax._gather_rows
 // copies the candidates' lm_head rows into a contiguous [P, d] table; the module
@@ -143,6 +143,49 @@ __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
     const uint32_t row = C ? (uint32_t)C[p] : p;
     store_vec<BF16>(dW, (size_t)row * vpr + c8, lo[u], hi[u]);
   }
+}
+
+// out[i, :] = W[idx[i], :] for i < n (rows of row_vecs 16-byte vectors, out rows
+// out_vecs apart); an index outside [0, V) gives a row of zeros and sets
+// kDevLabelRange in *status when status is given. 32 lanes per row, as the gather of
+// the step.
+__global__ __launch_bounds__(256) void k_gather_checked(const uint4* __restrict__ W, int64_t V,
+                                                        const int32_t* __restrict__ idx, int n,
+                                                        int row_vecs, uint4* __restrict__ out,
+                                                        int64_t out_vecs,
+                                                        int32_t* __restrict__ status) {
+  const int r = (int)blockIdx.x * kGatherRows + (int)(threadIdx.x >> 5);
+  if (r >= n) return;
+  const int l = threadIdx.x & 31;
+  const int64_t c = idx[r];
+  uint4* dst = out + (int64_t)r * out_vecs;
+  if (c < 0 || c >= V) {
+    for (int v = l; v < row_vecs; v += 32) dst[v] = make_uint4(0, 0, 0, 0);
+    if (status && l == 0) atomicOr(status, kDevLabelRange);
+    return;
+  }
+  const uint4* src = W + c * row_vecs;
+  // kInFlight vectors per lane per round, every load before the first store.
+  constexpr int kInFlight = 8;
+  for (int v0 = l; v0 < row_vecs; v0 += 32 * kInFlight) {
+    uint4 b[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u)
+      b[u] = v0 + 32 * u < row_vecs ? src[v0 + 32 * u] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u)
+      if (v0 + 32 * u < row_vecs) dst[v0 + 32 * u] = b[u];
+  }
+}
+
+hipError_t launch_gather_checked(const void* W, int64_t V, const int32_t* idx, int n,
+                                 int row_bytes, void* out, int64_t out_row_bytes,
+                                 int32_t* status, hipStream_t s) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_gather_checked, dim3((n + kGatherRows - 1) / kGatherRows), dim3(256), 0,
+                       s, static_cast<const uint4*>(W), V, idx, n, row_bytes / 16,
+                       static_cast<uint4*>(out), out_row_bytes / 16, status);
+  return hipGetLastError();
 }
 
 hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stride,

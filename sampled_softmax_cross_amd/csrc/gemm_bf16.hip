@@ -37,17 +37,6 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// vmcnt(LPS * min(after, I)), chosen at run time among compile-time immediates.
-template <int LPS, int I>
-__device__ __forceinline__ void wait_after(int after) {
-  if constexpr (I <= 0) {
-    vm_wait<0>();
-  } else {
-    if (after >= I) vm_wait<LPS * I>();
-    else wait_after<LPS, I - 1>(after);
-  }
-}
-
 // LDS chunk (16 B) holding chunk `ch` of r-major row `row` (SK / 8 chunks per row).
 template <int SK>
 __device__ __forceinline__ int rm_swizzle(int row) {
@@ -79,8 +68,8 @@ struct DmaTile {
   static_assert((R * SK) % (512 * NW) == 0 && (!KMAJ || R % 128 == 0 || R == 192), "tile shape");
   static constexpr int kN = R * SK / (512 * NW);  // DMA instructions per wave per stage
   int off[kN];  // byte offset of the lane's chunk from the tile origin
-  int kk[kN];   // k of the lane's chunk (r-major) or row (k-major), for the k clip
-  int rr[kN];   // row (r-major) or first column (k-major) of the lane's chunk
+  int kr[kN];   // (k << 16) | row of the lane's chunk, for the clip: k of the chunk
+                // (r-major) or its row (k-major), and its row (r-major) or first column
   int w;        // index of this wave among the NW that fill the tile
   __device__ __forceinline__ void init(int64_t ld, int wave) {
     const int lane = threadIdx.x & 63;
@@ -96,8 +85,7 @@ struct DmaTile {
         k = q / (R / 8);
         r = ((q % (R / 8)) ^ km_swizzle<R>(k)) * 8;
       }
-      kk[i] = k;
-      rr[i] = r;
+      kr[i] = (k << 16) | r;
       off[i] = (int)((KMAJ ? (int64_t)k * ld + r : (int64_t)r * ld + k) * 2);
     }
   }
@@ -110,7 +98,7 @@ struct DmaTile {
     for (int i = 0; i < kN; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(tile + (w * kN + i) * 64), 16,
-          (kk[i] < k_valid && rr[i] < rows_valid) ? off[i] : kOOB, 0, 0, 0);
+          ((kr[i] >> 16) < k_valid && (kr[i] & 0xffff) < rows_valid) ? off[i] : kOOB, 0, 0, 0);
   }
 };
 
@@ -143,9 +131,11 @@ __device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int
 // u = blockIdx.x, blockIdx.x + gridDim.x, ... and streams their k-stages through one
 // NS-deep LDS ring without a break between units: the first stages of the next unit
 // are already in flight while the current unit finishes and stores its tile.
-// BM x BN tile per unit, WGM x WGN waves; OCC workgroups share a CU.
+// BM x BN tile per unit, WGM x WGN waves; OCC workgroups share a CU. The A operand
+// has an NS-deep ring, the B operand an NSB-deep one (NSB <= NS): an operand that
+// streams from HBM can run further ahead than one that stays in the caches.
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
-          int SK>
+          int SK, int NSB>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ Cout, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t kps,
@@ -153,12 +143,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int STAGE = (BM + BN) * SK / 8;  // uint4 per stage
-  constexpr int A_OFF = BM * SK / 8;          // B tile offset in a stage (uint4)
-  constexpr int LPS = (BM + BN) * SK / (512 * NW);  // DMA instructions per wave per stage
-  constexpr int KS = SK / 16;                       // MFMA k-steps per stage
-  static_assert((SK == 32 || SK == 64) && NS >= 2 && LPS * (NS - 1) < 64, "pipeline shape");
-  __shared__ uint4 lds[NS * STAGE];
+  constexpr int A_SLOT = BM * SK / 8;  // uint4 per A stage
+  constexpr int B_SLOT = BN * SK / 8;  // uint4 per B stage
+  constexpr int LA = BM * SK / (512 * NW), LB = BN * SK / (512 * NW);  // DMA per wave
+  constexpr int KS = SK / 16;  // MFMA k-steps per stage
+  // Each step issues B, then A. Waiting for stage g + 1 leaves in flight what was issued
+  // after its later half: one A group when B runs shallower, plus whole steps.
+  constexpr int WAIT = NSB < NS ? LA + (NSB - 2) * (LA + LB) : (NS - 2) * (LA + LB);
+  constexpr int WAIT0 = (NSB - 1) * LB + (NS - 1) * LA;  // prologue: stage 0 landed
+  static_assert((SK == 32 || SK == 64) && NSB >= 2 && NSB <= NS && WAIT0 < 64, "pipeline shape");
+  __shared__ uint4 lds[NS * A_SLOT + NSB * B_SLOT];
+  uint4* const aring = lds;
+  uint4* const bring = lds + NS * A_SLOT;
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -191,22 +187,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   DmaTile<BN, B_KM, NW, SK> tb;
   ta.init(lda, wid);
   tb.init(ldb, wid);
-  // Issue cursor: unit iu, stage is of that unit. Past the last unit, stages are
-  // issued fully clipped (zeros, no memory traffic) so every wait count is constant.
-  int iu = 0, is = 0;
-  Unit ic = unit(0);
-  auto issue_next = [&](int slot_idx) {
-    uint4* slot = lds + slot_idx * STAGE;
-    const int64_t k0 = ic.kb + (int64_t)is * SK;
-    const bool live = iu < my_units;
-    const int64_t kv = live ? ic.ke - k0 : 0;
-    ta.issue(A_KM ? A + k0 * lda + ic.m0 : A + ic.m0 * lda + k0, M - ic.m0, kv, slot);
-    tb.issue(B_KM ? B + k0 * ldb + ic.n0 : B + ic.n0 * ldb + k0, N - ic.n0, kv, slot + A_OFF);
-    if (++is == nk) {
-      is = 0;
-      ++iu;
-      if (iu < my_units) ic = unit(iu);
+  // Issue cursors (unit iu, stage is of that unit), one per operand. Past the last unit,
+  // stages are issued fully clipped (zeros, no memory traffic) so every wait count is
+  // constant.
+  struct Cursor {
+    int iu, is;
+    Unit c;
+  };
+  Cursor ca{0, 0, unit(0)}, cb = ca;
+  auto advance = [&](Cursor& q) {
+    if (++q.is == nk) {
+      q.is = 0;
+      ++q.iu;
+      if (q.iu < my_units) q.c = unit(q.iu);
     }
+  };
+  auto issue_a = [&](int slot_idx) {
+    const int64_t k0 = ca.c.kb + (int64_t)ca.is * SK;
+    const int64_t kv = ca.iu < my_units ? ca.c.ke - k0 : 0;
+    ta.issue(A_KM ? A + k0 * lda + ca.c.m0 : A + ca.c.m0 * lda + k0, M - ca.c.m0, kv,
+             aring + slot_idx * A_SLOT);
+    advance(ca);
+  };
+  auto issue_b = [&](int slot_idx) {
+    const int64_t k0 = cb.c.kb + (int64_t)cb.is * SK;
+    const int64_t kv = cb.iu < my_units ? cb.c.ke - k0 : 0;
+    tb.issue(B_KM ? B + k0 * ldb + cb.c.n0 : B + cb.c.n0 * ldb + k0, N - cb.c.n0, kv,
+             bring + slot_idx * B_SLOT);
+    advance(cb);
   };
 
   const int arow = wm * WM;  // wave's first row / column in the tile
@@ -214,14 +222,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   const int l32 = lane & 31;
   bf16x8_t fa[2][TM], fb[2][TN];
   auto read_frags = [&](int g, int ks, int buf) {
-    const uint4* slot = lds + (g % NS) * STAGE;
+    const uint4* as = aring + (g % NS) * A_SLOT;
+    const uint4* bs = bring + (g % NSB) * B_SLOT;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      fa[buf][i] = read_frag<BM, A_KM, SK>(slot, arow + i * 32 + l32, arow + i * 32, ks, lane);
+      fa[buf][i] = read_frag<BM, A_KM, SK>(as, arow + i * 32 + l32, arow + i * 32, ks, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      fb[buf][j] =
-          read_frag<BN, B_KM, SK>(slot + A_OFF, bcol + j * 32 + l32, bcol + j * 32, ks, lane);
+      fb[buf][j] = read_frag<BN, B_KM, SK>(bs, bcol + j * 32 + l32, bcol + j * 32, ks, lane);
   };
   f32x16_t acc[TM][TN];
   auto mfma_step = [&](int buf) {
@@ -245,10 +253,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     if (kReads > pairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - pairs, 0);
   };
 
-  // Prologue: fill every slot, wait for global stage 0, fetch its first fragments.
+  // Prologue: fill every slot (B then A per stage), wait for global stage 0, fetch its
+  // first fragments.
 #pragma unroll
-  for (int s = 0; s < NS; ++s) issue_next(s);
-  vm_wait<LPS * (NS - 1)>();
+  for (int s = 0; s < NS; ++s) {
+    if (s < NSB) issue_b(s);
+    issue_a(s);
+  }
+  vm_wait<WAIT0>();
   __syncthreads();
   read_frags(0, 0, 0);
 
@@ -269,11 +281,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
         mfma_step(q & 1);
         interleave();
       }
-      // Stage g + 1 becomes visible; slot g % NS has no readers left (all of its
-      // fragment sets are in registers), so it takes stage g + NS.
-      vm_wait<LPS * (NS - 2)>();
+      // Stage g + 1 becomes visible; the slots of stage g have no readers left (all
+      // of their fragment sets are in registers), so they take stages g + NSB (B) and
+      // g + NS (A).
+      vm_wait<WAIT>();
       __syncthreads();
-      issue_next(g % NS);
+      issue_b(g % NSB);
+      issue_a(g % NS);
       // Last k-step of stage g, with the first reads of stage g + 1 in its shadow
       // (after the last stage these read a slot that is never used: in bounds, ignored).
       read_frags(g + 1, 0, 0);
@@ -285,20 +299,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   }
 }
 
-#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK)                          \
-  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK>(          \
+#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB)                     \
+  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB>(     \
       const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
       int64_t, int64_t, int);
-SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64)
-SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64)
-SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64)
-SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32)
-SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32)
-SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32)
+SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2)
+SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64, 2)
+SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2)
+SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32, 3)
+SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32, 3)
+SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32, 3)
 #undef SCE_GEMM16_INST
 
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
-          int SK>
+          int SK, int NSB>
 static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   const int splits = a.splits > 0 ? a.splits : 1;
   int64_t kps = (a.K + splits - 1) / splits;
@@ -312,7 +326,7 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   // workgroup's units on one XCD), or one per unit when there are fewer.
   const int slots = cu_count() * OCC;
   const int grid = (int)(units < slots ? units : slots);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK>),
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK, NSB>),
                      dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, s, static_cast<const bf16_t*>(a.A), a.lda,
                      static_cast<const bf16_t*>(a.B), a.ldb, a.C, a.ldc, a.M, a.N, a.K, kps,
                      a.split_stride, splits);
@@ -370,16 +384,16 @@ int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {
-    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64>(a, s);
+    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2>(a, s);
     case Gemm::DX:
       if (dx_wide(a.N))
         return a.splits > 1
-                   ? run16<kWideM, kWideN, 4, 2, false, true, kOutF32Split, 2, 1, 64>(a, s)
-                   : run16<kWideM, kWideN, 4, 2, false, true, kOutBF16, 2, 1, 64>(a, s);
+                   ? run16<kWideM, kWideN, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2>(a, s)
+                   : run16<kWideM, kWideN, 4, 2, false, true, kOutBF16, 2, 1, 64, 2>(a, s);
       return a.splits > 1
-                 ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32>(a, s)
-                 : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32>(a, s);
-    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc, 32>(a, s);
+                 ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32, 3>(a, s)
+                 : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32, 3>(a, s);
+    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc, 32, 3>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -65,6 +65,15 @@ hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stri
                                const int32_t* vocab_pos, const int32_t* C, int rows, int V, int d,
                                bool bf16, void* dW, const LossOut* fin, hipStream_t s);
 
+// Caller-given label positions for the CE alone: copies with positions outside
+// [-1, P) replaced by -1 (flagged in the status counter), N counted, counters set.
+hipError_t launch_ce_prep(const int32_t* tpos_in, const int32_t* ppos_in, int T, int P,
+                          int32_t* tpos, int32_t* ppos, int32_t* counters, hipStream_t s);
+// out[i, :] = W[idx[i], :] (zeros and kDevLabelRange in *status for idx outside [0, V)).
+hipError_t launch_gather_checked(const void* W, int64_t V, const int32_t* idx, int n,
+                                 int row_bytes, void* out, int64_t out_row_bytes,
+                                 int32_t* status, hipStream_t s);
+
 // Row-wise cross-entropy forward/backward over Z [T, ldz] (P valid columns), in place.
 hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
                           const int32_t* target_pos, const int32_t* prefix_pos,

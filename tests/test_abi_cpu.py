@@ -85,3 +85,34 @@ def test_forward_backward_host_checks(lib):
     b = lib.sce_build_candidates
     assert b(fake, None, 4, 16, 0, 3, 0, fake, None, fake, None, None, fake, 1 << 30, None) == 1  # P = 0
     assert b(fake, None, 4, 16, 4, 2, 0, fake, None, fake, None, None, fake, 1 << 30, None) == 1  # gcd
+
+
+def test_building_block_host_checks(lib):
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    out = ctypes.c_size_t(0)
+    assert lib.sce_ce_rows_workspace_size(100, ctypes.byref(out)) == 0 and out.value >= 100 * 12
+    assert lib.sce_ce_rows_workspace_size(-1, ctypes.byref(out)) == 1
+    assert lib.sce_ce_rows_workspace_size(4, None) == 1
+    ce = dict(Z=fake, ldz=16, T=4, P=10, dt=1, tp=fake, pp=None, loss=fake, rl=None, lse=None,
+              aux=None, ws=None, wsb=0, s=None)
+
+    def cer(**kw):
+        a = dict(ce, **kw)
+        return lib.sce_ce_rows(*a.values())
+
+    assert cer() == 2                           # no workspace
+    assert cer(ldz=12) == 1                     # ldz % 8 != 0
+    assert cer(ldz=8) == 1                      # ldz < P
+    assert cer(P=0) == 1
+    assert cer(dt=7) == 1
+    assert cer(loss=None) == 1
+    assert cer(tp=None) == 1
+    assert cer(Z=ctypes.c_void_p((1 << 20) + 4)) == 1  # misaligned
+    assert cer(ws=fake, wsb=16) == 2                   # too small
+    g = lib.sce_gather_rows
+    assert g(fake, 16, 12, fake, 4, 1, fake, 16, None, None) == 1   # d % 8 != 0
+    assert g(fake, 16, 16, fake, 4, 1, fake, 8, None, None) == 1    # ld_out < d
+    assert g(fake, 16, 16, None, 4, 1, fake, 16, None, None) == 1   # null indices
+    assert g(fake, 0, 16, fake, 4, 1, fake, 16, None, None) == 1    # empty table
+    assert g(fake, 16, 16, fake, 4, 5, fake, 16, None, None) == 1   # dtype
+    assert g(None, 16, 16, None, 0, 1, None, 16, None, None) == 0   # nothing to gather

@@ -112,6 +112,36 @@ def test_matches_torch_cross_entropy(seed, T, d, V, P, prefix, ign):
     np.testing.assert_allclose(np.exp(z - L[:, None]).sum(axis=1), 1.0, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed,T,P,prefix,ign", [(5, 40, 257, True, 0.1), (6, 7, 3, False, 0.0),
+                                                 (7, 25, 64, True, 0.5)])
+def test_ce_rows_matches_torch_on_logits(seed, T, P, prefix, ign):
+    """The logits-level entry against PyTorch float64 cross_entropy and autograd on the
+    logits themselves (duplicate target/prefix positions included)."""
+    r = np.random.default_rng(seed)
+    z = r.standard_normal((T, P)) * 3.0
+    tpos = r.integers(0, P, T)
+    tpos[r.random(T) < ign] = -1
+    ppos = None
+    if prefix:
+        ppos = r.integers(0, P, T)
+        ppos[r.random(T) < ign] = -1
+        ppos[0] = tpos[0] if tpos[0] >= 0 else 0    # a duplicated label
+    loss, g, L, row_loss, N = ce.ce_rows(z, tpos, ppos)
+    zt = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+    s = torch.nn.functional.cross_entropy(zt, torch.as_tensor(tpos), ignore_index=-1, reduction="sum")
+    n = int((tpos >= 0).sum())
+    if ppos is not None:
+        s = s + torch.nn.functional.cross_entropy(zt, torch.as_tensor(ppos), ignore_index=-1,
+                                                  reduction="sum")
+        n += int((ppos >= 0).sum())
+    (s / n).backward()
+    assert N == n
+    assert math.isclose(loss, (s / n).item(), rel_tol=1e-12)
+    np.testing.assert_allclose(g, zt.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(L, torch.logsumexp(zt.detach(), dim=1).numpy(), rtol=1e-14, atol=0)
+    assert math.isclose(row_loss.sum() / n, loss, rel_tol=1e-12)
+
+
 def test_central_finite_differences():
     """d loss / d x and d loss / d W against central differences (h = 1e-6), with a
     duplicated label (prefix == target), a dropped prefix and an ignored target."""
