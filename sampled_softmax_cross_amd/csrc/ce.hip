@@ -239,6 +239,96 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
   }
 }
 
+// Short rows (at most 64 * VPT vectors): one wave per row, four rows per workgroup,
+// the (max, sum) merge by shuffles only (no LDS, no barrier). The same arithmetic as
+// k_ce_rows with exp(Z - m_lane) kept per element.
+template <typename TZ, int VPT>
+__global__ __launch_bounds__(256) void k_ce_rows_wave(TZ* __restrict__ Z, int64_t ldz, int P,
+                                                      int T, const int32_t* __restrict__ tpos,
+                                                      const int32_t* __restrict__ ppos,
+                                                      const int32_t* __restrict__ counters,
+                                                      float* __restrict__ row_loss,
+                                                      float* __restrict__ row_lse) {
+  using RV = RowVec<TZ>;
+  constexpr int E = RV::kElems;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = (int)blockIdx.x * 4 + (int)(threadIdx.x / kWave);
+  if (t >= T) return;  // a whole wave
+  TZ* row = Z + (int64_t)t * ldz;
+  uint4* rowv = reinterpret_cast<uint4*>(row);
+  const int nvec = (int)(ldz / E);
+  const int tp = tpos[t];
+  const int pp = ppos[t];
+  // the label logits, read before any lane writes the row back
+  const float zt = tp >= 0 ? RV::load1(row + tp) : 0.f;
+  const float zp = pp >= 0 ? RV::load1(row + pp) : 0.f;
+  float v[VPT][E];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = lane + k * kWave;
+    if (i < nvec) {
+      RV::unpack(rowv[i], v[k]);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (i * E + e >= P) v[k][e] = -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[k][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmaxf(m, v[k][e]);
+  }
+  const float mb = m == -INFINITY ? 0.f : m * kLog2e;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      v[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[k][e], kLog2e, -mb));
+      s += v[k][e];
+    }
+  float M = m, S = s;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, kWave);
+    const float s2 = __shfl_xor(S, o, kWave);
+    merge_ms(M, S, m2, s2);
+  }
+  const float L = M + __builtin_amdgcn_logf(S) * kLn2;  // logf here is log2
+  const int N = counters[kNumLabels];
+  const float inv = N > 0 ? 1.0f / (float)N : 0.f;
+  const int nt = (tp >= 0) + (pp >= 0);
+  const float scale = m == -INFINITY ? 0.f
+                                     : (float)nt * inv * __builtin_amdgcn_exp2f((m - L) * kLog2e);
+  const int vt = tp >= 0 ? tp / E : -1;
+  const int vp = pp >= 0 ? pp / E : -1;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int i = lane + k * kWave;
+    if (i < nvec) {
+      float g[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) g[e] = v[k][e] * scale;
+      if (i == vt || i == vp) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int j = i * E + e;
+          g[e] -= (float)((j == tp) + (j == pp)) * inv;
+        }
+      }
+      rowv[i] = RV::pack(g);
+    }
+  }
+  if (lane == 0) {
+    float l = 0.f;
+    if (tp >= 0) l += L - zt;
+    if (pp >= 0) l += L - zp;
+    row_loss[t] = l;
+    if (row_lse) row_lse[t] = L;
+  }
+}
+
 // Rows too long for registers: two sweeps over HBM (online (max, sum), then write).
 template <typename TZ, int NT>
 __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64_t ldz, int P,
@@ -338,7 +428,18 @@ static void launch_ce_typed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
                             float* loss, int64_t* aux, hipStream_t s) {
   constexpr int E = RowVec<TZ>::kElems;
   const int64_t nvec = ldz / E;
-  if (nvec <= 256 * 16) {
+  if (nvec <= kWave * 4) {
+    const int vpt = (int)((nvec + kWave - 1) / kWave);
+    const dim3 grid((T + 3) / 4), block(256);
+    if (vpt <= 1)
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 1>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+    else if (vpt == 2)
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 2>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+    else if (vpt == 3)
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 3>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+    else
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 4>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+  } else if (nvec <= 256 * 16) {
     launch_ce_nt<TZ, 256>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse,
                           loss, aux, s);
   } else if (nvec <= 512 * 16) {
