@@ -133,9 +133,11 @@ __device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int
 // are already in flight while the current unit finishes and stores its tile.
 // BM x BN tile per unit, WGM x WGN waves; OCC workgroups share a CU. The A operand
 // has an NS-deep ring, the B operand an NSB-deep one (NSB <= NS): an operand that
-// streams from HBM can run further ahead than one that stays in the caches.
+// streams from HBM can run further ahead than one that stays in the caches. IL: issue
+// the fragment reads one per MFMA (sched_group_barrier) instead of leaving the
+// interleave to the compiler; which is faster depends on the product (measured).
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
-          int SK, int NSB>
+          int SK, int NSB, bool IL>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
     void* __restrict__ Cout, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t kps,
@@ -147,14 +149,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   constexpr int B_SLOT = BN * SK / 8;  // uint4 per B stage
   constexpr int LA = BM * SK / (512 * NW), LB = BN * SK / (512 * NW);  // DMA per wave
   constexpr int KS = SK / 16;  // MFMA k-steps per stage
-  // Each step issues B, then A. Waiting for stage g + 1 leaves in flight what was issued
-  // after its later half: one A group when B runs shallower, plus whole steps.
+  // Each step issues A then B (equal depths) or B then A (B shallower). Waiting for
+  // stage g + 1 leaves in flight what was issued after its later half: whole steps,
+  // plus one A group when B runs shallower.
   constexpr int WAIT = NSB < NS ? LA + (NSB - 2) * (LA + LB) : (NS - 2) * (LA + LB);
   constexpr int WAIT0 = (NSB - 1) * LB + (NS - 1) * LA;  // prologue: stage 0 landed
   static_assert((SK == 32 || SK == 64) && NSB >= 2 && NSB <= NS && WAIT0 < 64, "pipeline shape");
+  // Equal depths: stage s holds its A tile then its B tile (one slot of A_SLOT + B_SLOT);
+  // otherwise an A ring followed by a B ring.
   __shared__ uint4 lds[NS * A_SLOT + NSB * B_SLOT];
-  uint4* const aring = lds;
-  uint4* const bring = lds + NS * A_SLOT;
+  auto a_slot = [&](int i) { return lds + (NSB == NS ? i * (A_SLOT + B_SLOT) : i * A_SLOT); };
+  auto b_slot = [&](int i) {
+    return lds + (NSB == NS ? i * (A_SLOT + B_SLOT) + A_SLOT : NS * A_SLOT + i * B_SLOT);
+  };
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -194,7 +201,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     int iu, is;
     Unit c;
   };
-  Cursor ca{0, 0, unit(0)}, cb = ca;
+  Cursor ca{0, 0, unit(0)};
+  Cursor cb = ca;  // B's cursor when NSB < NS
   auto advance = [&](Cursor& q) {
     if (++q.is == nk) {
       q.is = 0;
@@ -206,15 +214,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     const int64_t k0 = ca.c.kb + (int64_t)ca.is * SK;
     const int64_t kv = ca.iu < my_units ? ca.c.ke - k0 : 0;
     ta.issue(A_KM ? A + k0 * lda + ca.c.m0 : A + ca.c.m0 * lda + k0, M - ca.c.m0, kv,
-             aring + slot_idx * A_SLOT);
+             a_slot(slot_idx));
     advance(ca);
   };
   auto issue_b = [&](int slot_idx) {
     const int64_t k0 = cb.c.kb + (int64_t)cb.is * SK;
     const int64_t kv = cb.iu < my_units ? cb.c.ke - k0 : 0;
     tb.issue(B_KM ? B + k0 * ldb + cb.c.n0 : B + cb.c.n0 * ldb + k0, N - cb.c.n0, kv,
-             bring + slot_idx * B_SLOT);
+             b_slot(slot_idx));
     advance(cb);
+  };
+  // With equal depths both operands of a stage go out together from one cursor, A then
+  // B (the wait counts are symmetric then), which keeps the second cursor's registers
+  // free.
+  auto issue_stage = [&](int slot_idx) {
+    const int64_t k0 = ca.c.kb + (int64_t)ca.is * SK;
+    const int64_t kv = ca.iu < my_units ? ca.c.ke - k0 : 0;
+    ta.issue(A_KM ? A + k0 * lda + ca.c.m0 : A + ca.c.m0 * lda + k0, M - ca.c.m0, kv,
+             a_slot(slot_idx));
+    tb.issue(B_KM ? B + k0 * ldb + ca.c.n0 : B + ca.c.n0 * ldb + k0, N - ca.c.n0, kv,
+             b_slot(slot_idx));
+    advance(ca);
   };
 
   const int arow = wm * WM;  // wave's first row / column in the tile
@@ -222,8 +242,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   const int l32 = lane & 31;
   bf16x8_t fa[2][TM], fb[2][TN];
   auto read_frags = [&](int g, int ks, int buf) {
-    const uint4* as = aring + (g % NS) * A_SLOT;
-    const uint4* bs = bring + (g % NSB) * B_SLOT;
+    const uint4* as = a_slot(g % NS);
+    const uint4* bs = b_slot(g % NSB);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
       fa[buf][i] = read_frag<BM, A_KM, SK>(as, arow + i * 32 + l32, arow + i * 32, ks, lane);
@@ -239,26 +259,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
   };
-  // Issue order inside a k-step: MFMA, fragment read, MFMA, read, ..., then MFMAs.
   constexpr int kReads = (A_KM ? 2 : 1) * TM + (B_KM ? 2 : 1) * TN;
   constexpr int kMfma = TM * TN;
   auto interleave = [&]() {
-    constexpr int pairs = kReads < kMfma ? kReads : kMfma;
+    if constexpr (IL) {
+      constexpr int pairs = kReads < kMfma ? kReads : kMfma;
 #pragma unroll
-    for (int g = 0; g < pairs; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      for (int g = 0; g < pairs; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      if (kMfma > pairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - pairs, 0);
+      if (kReads > pairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - pairs, 0);
     }
-    if (kMfma > pairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - pairs, 0);
-    if (kReads > pairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - pairs, 0);
   };
 
   // Prologue: fill every slot (B then A per stage), wait for global stage 0, fetch its
   // first fragments.
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (s < NSB) issue_b(s);
-    issue_a(s);
+    if constexpr (NSB == NS) {
+      issue_stage(s);
+    } else {
+      if (s < NSB) issue_b(s);
+      issue_a(s);
+    }
   }
   vm_wait<WAIT0>();
   __syncthreads();
@@ -286,8 +311,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
       // g + NS (A).
       vm_wait<WAIT>();
       __syncthreads();
-      issue_b(g % NSB);
-      issue_a(g % NS);
+      if constexpr (NSB == NS) {
+        issue_stage(g % NS);
+      } else {
+        issue_b(g % NSB);
+        issue_a(g % NS);
+      }
       // Last k-step of stage g, with the first reads of stage g + 1 in its shadow
       // (after the last stage these read a slot that is never used: in bounds, ignored).
       read_frags(g + 1, 0, 0);
@@ -299,20 +328,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   }
 }
 
-#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB)                     \
-  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB>(     \
+#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL)                 \
+  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL>( \
       const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
       int64_t, int64_t, int);
-SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2)
-SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64, 2)
-SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2)
-SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32, 3)
-SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32, 3)
-SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32, 3)
+SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2, true)
+SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64, 2, false)
+SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2, false)
+SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32, 3, true)
+SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32, 3, true)
+SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32, 3, true)
 #undef SCE_GEMM16_INST
 
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
-          int SK, int NSB>
+          int SK, int NSB, bool IL>
 static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   const int splits = a.splits > 0 ? a.splits : 1;
   int64_t kps = (a.K + splits - 1) / splits;
@@ -326,7 +355,7 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   // workgroup's units on one XCD), or one per unit when there are fewer.
   const int slots = cu_count() * OCC;
   const int grid = (int)(units < slots ? units : slots);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK, NSB>),
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK, NSB, IL>),
                      dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, s, static_cast<const bf16_t*>(a.A), a.lda,
                      static_cast<const bf16_t*>(a.B), a.ldb, a.C, a.ldc, a.M, a.N, a.K, kps,
                      a.split_stride, splits);
@@ -384,16 +413,16 @@ int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {
-    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2>(a, s);
+    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2, true>(a, s);
     case Gemm::DX:
       if (dx_wide(a.N))
         return a.splits > 1
-                   ? run16<kWideM, kWideN, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2>(a, s)
-                   : run16<kWideM, kWideN, 4, 2, false, true, kOutBF16, 2, 1, 64, 2>(a, s);
+                   ? run16<kWideM, kWideN, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2, false>(a, s)
+                   : run16<kWideM, kWideN, 4, 2, false, true, kOutBF16, 2, 1, 64, 2, false>(a, s);
       return a.splits > 1
-                 ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32, 3>(a, s)
-                 : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32, 3>(a, s);
-    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc, 32, 3>(a, s);
+                 ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32, 3, true>(a, s)
+                 : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32, 3, true>(a, s);
+    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc, 32, 3, true>(a, s);
   }
   return hipErrorInvalidValue;
 }
