@@ -63,7 +63,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     p.wc = take(P > 0 ? (size_t)P * p.ldwc * es : 0);
     p.z = take((size_t)T * p.ldz * es);
     if (dtype == SCE_BF16) {
-      p.splits = gemm_bf16_splits(p.Peff, d, T, 8, false);
+      p.splits = gemm_bf16_dw_splits(p.Peff, d, T);
       p.dx_splits = gemm_bf16_dx_splits(T, d, p.Peff);
     } else {
       p.splits = gemm_f32_splits(p.Peff, d, T);

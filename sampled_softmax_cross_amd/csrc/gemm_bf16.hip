@@ -145,6 +145,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles are whole 32x32 MFMA blocks");
   constexpr int A_SLOT = BM * SK / 8;  // uint4 per A stage
   constexpr int B_SLOT = BN * SK / 8;  // uint4 per B stage
   constexpr int LA = BM * SK / (512 * NW), LB = BN * SK / (512 * NW);  // DMA per wave
@@ -337,7 +338,7 @@ SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64, 2, false)
 SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2, false)
 SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32, 3, true)
 SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32, 3, true)
-SCE_GEMM16_INST(128, 256, 2, 2, true, true, kOutF32Split, 3, 2, 32, 3, true)
+SCE_GEMM16_INST(256, 256, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false)
 #undef SCE_GEMM16_INST
 
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
@@ -370,17 +371,16 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
 //  * dX, N a multiple of 192: 256 x 192 tiles, 8 waves (4 x 2, 64 x 96 each), one
 //    workgroup per CU, two stages of 64 k: N = 768 gives 4 column tiles, so M = 16384
 //    fills the 256 CUs exactly once;
-//  * dX otherwise, and dW: 128 x 256 tiles with two workgroups per CU (their epilogues
-//    and barrier stalls interleave), three stages of 32 k, dX with 8 waves (64 x 64
-//    each) and dW with 4 (64 x 128 each).
+//  * dX otherwise: 128 x 256 tiles with two workgroups per CU (their epilogues and
+//    barrier stalls interleave), three stages of 32 k, 8 waves of 64 x 64;
+//  * dW: 256 x 256 tiles, 8 waves (4 x 2, 64 x 128 each), two stages of 64 k, fragment
+//    reads scheduled by the compiler (13-20% faster than the 128 x 256 two-per-CU
+//    configuration at P = 10240 ... 50304, T = 16384 ... 49152).
 constexpr int kTileM = 128, kTileN = 256, kOcc = 2;
 constexpr int kWideM = 256, kWideN = 192;
+constexpr int kDwM = 256, kDwN = 256;
 static bool dx_wide(int64_t N) { return N % kWideN == 0; }
 
-// Smallest k-split whose units fill at least 85% of the workgroup slots of the rounds
-// they occupy (wave quantisation), keeping at least 1024 k per split. When a split
-// needs an extra reduction pass (dX), it is only taken once the unsplit product
-// already fills a full round of slots.
 static int splits_for(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass,
                       int bm, int bn, int occ) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
@@ -402,8 +402,28 @@ static int splits_for(int64_t M, int64_t N, int64_t K, int max_splits, bool spli
   return best;
 }
 
-int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass) {
-  return splits_for(M, N, K, max_splits, split_costs_pass, kTileM, kTileN, kOcc);
+// dW (M = P, N = d, K = T: few output tiles, long k): the k-split that minimises an
+// estimate of the product's time. Units run in whole rounds of one per CU, each round
+// streaming ceil(K / s) k at about 1.0 PFLOP/s over the chip (measured full-round rate of
+// this configuration); every split adds an fp32 partial of M x N that is written here
+// and read once by the reduction (8 bytes per element at about 5 TB/s).
+int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + kDwM - 1) / kDwM) * ((N + kDwN - 1) / kDwN);
+  const int64_t slots = cu_count();
+  const double ns_per_k = 2.0 * kDwM * kDwN * (double)slots / 1.0e6;  // one round, 1e15 FLOP/s
+  const double ns_per_partial = 8.0 * (double)M * (double)N / 5.0e3;  // 5e12 B/s
+  int best = 1;
+  double best_ns = 0.0;
+  for (int s = 1; s <= 8; ++s) {
+    if (s > 1 && K / s < 1024) break;
+    const int64_t rounds = (tiles * s + slots - 1) / slots;
+    const double ns = (double)rounds * (double)((K + s - 1) / s) * ns_per_k + s * ns_per_partial;
+    if (s == 1 || ns < best_ns) {
+      best_ns = ns;
+      best = s;
+    }
+  }
+  return best;
 }
 
 int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K) {
@@ -422,7 +442,7 @@ hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
       return a.splits > 1
                  ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32, 3, true>(a, s)
                  : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32, 3, true>(a, s);
-    case Gemm::DW: return run16<kTileM, kTileN, 2, 2, true, true, kOutF32Split, 3, kOcc, 32, 3, true>(a, s);
+    case Gemm::DW: return run16<kDwM, kDwN, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -91,13 +91,12 @@ struct GemmArgs {
   void* C;
   int64_t ldc;
   int64_t M, N, K;
-  int splits;            // split-K factor (DW only)
-  int64_t split_stride;  // elements between split slabs of C (DW only)
+  int splits;            // split-K factor (fp32 partial slabs when > 1)
+  int64_t split_stride;  // elements between split slabs of C
 };
-// k-split factor for a GEMM of this shape (1 = no split). bf16 products; the fp32
-// products use gemm_f32_splits.
-int gemm_bf16_splits(int64_t M, int64_t N, int64_t K, int max_splits, bool split_costs_pass);
-// k-split of the bf16 dX product, for the tile shape its launch uses.
+// k-splits (1 = no split) of the bf16 dW and dX products, for the tile shapes their
+// launches use; the fp32 products use gemm_f32_splits.
+int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K);
 int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K);
 int gemm_f32_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Gemm kind, bool bf16, const GemmArgs& a, hipStream_t s);
