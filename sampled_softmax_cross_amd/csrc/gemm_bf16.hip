@@ -179,14 +179,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     int64_t m0, n0, kb, ke;
   };
   auto unit = [&](int i) {
-    const int u = (int)blockIdx.x + i * G;
-    const int t = u % ntiles;
-    int tm, tn;
-    tile_of(t, nby, nbx, tm, tn);
+    int tm, tn, sp;
+    unit_of((int)blockIdx.x + i * G, nby, nbx, splits, tm, tn, sp);
     Unit c;
     c.m0 = (int64_t)tm * BM;
     c.n0 = (int64_t)tn * BN;
-    c.kb = (int64_t)(u / ntiles) * kps;
+    c.kb = (int64_t)sp * kps;
     c.ke = K < c.kb + kps ? K : c.kb + kps;
     return c;
   };

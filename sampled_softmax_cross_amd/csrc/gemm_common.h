@@ -56,6 +56,34 @@ __device__ __forceinline__ void tile_of(int bid, int nby, int nbx, int& tm, int&
   tn = in / gsize;
 }
 
+// Tile and k-range of unit u among nby x nbx tiles x `splits` k-ranges. Units are
+// renumbered XCD-contiguously (workgroup ids are dealt round-robin over the XCDs) with the
+// k-range outermost, so each XCD works on one k-range. Within a k-range, tiles go
+// row-major when there are at most 4 column tiles (every column tile of a row shares the
+// row's A block, and they land on the same XCD), otherwise in groups of kGroupM rows.
+__device__ __forceinline__ void unit_of(int u, int nby, int nbx, int splits, int& tm, int& tn,
+                                        int& split) {
+  const int ntiles = nby * nbx;
+  const int total = ntiles * splits;
+  const int q = total / kNumXcd, rem = total % kNumXcd;
+  const int x = u % kNumXcd, i = u / kNumXcd;
+  const int lid = x < rem ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
+  split = lid / ntiles;
+  const int t = lid - split * ntiles;
+  if (nbx <= 4) {
+    tm = t / nbx;
+    tn = t - tm * nbx;
+    return;
+  }
+  const int per_group = kGroupM * nbx;
+  const int g = t / per_group;
+  const int first = g * kGroupM;
+  const int gsize = min(nby - first, kGroupM);
+  const int in = t - g * per_group;
+  tm = first + in % gsize;
+  tn = in / gsize;
+}
+
 // Compute units of the current device (cached per device; 256 when unknown).
 inline int cu_count() {
   static int counts[64] = {0};
