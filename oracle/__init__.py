@@ -8,9 +8,12 @@ generator, which holds none of the method's arithmetic.
 * ``candidates``: the candidate build, sequential plain C (``candidates.c``).
 * ``ce``: loss and gradients in float64 numpy, dense for small shapes and
   entry-by-entry ("sampled") for full-size shapes.
+* ``fp8``: the e4m3-operand variant of the step (e4m3 codec, power-of-two
+  per-tensor scales, bf16 logits) in float64 numpy.
 
 Every function states the passage of the pages it follows. Parity pins live in
 ``tests/test_oracle_*.py``; functions without an independent pin say so.
 """
 from .candidates import build_candidates, OracleError  # noqa: F401
 from . import ce  # noqa: F401
+from . import fp8  # noqa: F401
