@@ -52,11 +52,13 @@ typedef enum sce_status {
   SCE_EHIP = 3        /* a HIP launch failed (see hipGetLastError) */
 } sce_status;
 
-typedef enum sce_dtype { SCE_F32 = 0, SCE_BF16 = 1 } sce_dtype;
+/* SCE_E4M3 names the fp8 step (sampled_ce_forward_backward_fp8) in sce_workspace_size. */
+typedef enum sce_dtype { SCE_F32 = 0, SCE_BF16 = 1, SCE_E4M3 = 2 } sce_dtype;
 
 /* Device-detected conditions (bits of aux_out[3]). */
 #define SCE_DEV_TOO_MANY_TARGETS 1 /* distinct targets > P (the page asserts this never happens) */
 #define SCE_DEV_LABEL_RANGE 2      /* a target or prefix target outside [-1, V) */
+#define SCE_DEV_SCALE_RANGE 4      /* fp8 step: x not finite, or 0 < max|x| < 2^-100 */
 
 /* Limits checked on the host. */
 #define SCE_MAX_V_SAMPLED 131072 /* V limit when P > 0 (two candidate bitmaps held in LDS) */
@@ -142,6 +144,41 @@ SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, con
                                        int32_t* prefix_pos_out, float* row_lse_out,
                                        float* row_loss_out, int64_t* aux_out, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * sampled_ce_forward_backward_fp8 -- the same step with e4m3 (OCP E4M3, "e4m3fn")
+ * matrix-product operands. "sampled_softmax.py" keeps the lm_head as an e4m3 cache,
+ * gathers the candidate rows from it as e4m3 and multiplies with scaled fp8 products
+ * (SampledLoss rows / rows_t, SampledSoftmax._gather_rows); the scaling is not on the
+ * page, and this entry point takes per-tensor power-of-two scales:
+ *   s_x = the smallest power of two with max|x| <= 448 s_x, x8 = e4m3(x / s_x);
+ *   Z   = bf16( s_x w_scale (x8 W8_C^T) )                (fp32 accumulation);
+ *   L_t, the loss, N and the logit gradient g as in sampled_ce_forward_backward,
+ *         computed from these bf16 logits;
+ *   s_g = the smallest power of two with n_max / N <= 448 s_g (n_max = 2 when
+ *         prefix_targets is given, else 1; every |g| <= n_max / N), g8 = e4m3(g / s_g);
+ *   dX  = bf16( s_g w_scale (g8 W8_C) ),  dW_C = s_g s_x (g8^T x8),
+ *   dW [V, d] bf16 = dW_C in the rows of C, exactly zero elsewhere.
+ * e4m3 encodings round to nearest, ties to even.
+ *
+ *   x [T, d] bf16, d a multiple of 16.    W8 [V, d] e4m3 codes (the lm_head cache).
+ *   w_scale (host) > 0, finite: W ~ w_scale * W8.
+ *   targets, prefix_targets, P, stride, offset, loss, the position outputs,
+ *   row_lse_out, row_loss_out, aux_out: as in sampled_ce_forward_backward.
+ *   dX [T, d], dW [V, d] bf16, overwritten.
+ *   scales_out [2] float32 or NULL: {s_x, s_g}.
+ *   workspace: at least sce_workspace_size(T, d, V, P, SCE_E4M3) bytes, 256-byte aligned.
+ * x non-finite, or with 0 < max|x| < 2^-100, sets SCE_DEV_SCALE_RANGE in aux_out[3].
+ */
+SCE_API sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float w_scale,
+                                           const int64_t* targets, const int64_t* prefix_targets,
+                                           int64_t T, int64_t d, int64_t V, int64_t P,
+                                           int64_t stride, int64_t offset, float* loss, void* dX,
+                                           void* dW, int32_t* candidates_out,
+                                           int32_t* target_pos_out, int32_t* prefix_pos_out,
+                                           float* row_lse_out, float* row_loss_out,
+                                           int64_t* aux_out, float* scales_out, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /*
  * sce_ce_rows -- the fused cross-entropy forward/backward of the step on its own, in

@@ -130,7 +130,8 @@ def forward_backward(x, W8, w_scale, C, target_pos, prefix_pos=None):
     """Dense fp8 oracle. x [T,d] float64 (exact widening of the bf16 input), W8 [V,d]
     e4m3 codes, w_scale the float32 dequantisation scale, C the candidate classes
     (None: full softmax). Returns a dict: loss, dX [T,d], dW [V,d], L, row_loss,
-    z (bf16 logits), s_x, s_g, x8, g8."""
+    z (bf16 logits), s_x, s_g, x8, g8, N, and the values before their roundings:
+    z_exact (the scaled product) and g_scaled (g / s_g)."""
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
     W8 = np.asarray(W8, dtype=np.uint8)
@@ -140,7 +141,8 @@ def forward_backward(x, W8, w_scale, C, target_pos, prefix_pos=None):
     WCv = e4m3_decode(W8C)
     x8, s_x = quantize_x(x) if T else (np.zeros((0, d), np.uint8), 1.0)
     xv = e4m3_decode(x8)
-    z = bf16_round((s_x * w_scale) * (xv @ WCv.T))
+    z_exact = (s_x * w_scale) * (xv @ WCv.T)
+    z = bf16_round(z_exact)
     loss, g, L, row_loss, N = _ce.ce_rows(z, target_pos, prefix_pos)
     n_max = 2 if prefix_pos is not None else 1
     s_g = grad_scale(N, n_max)
@@ -154,7 +156,7 @@ def forward_backward(x, W8, w_scale, C, target_pos, prefix_pos=None):
     else:
         dW[np.asarray(C, dtype=np.int64)] = dWC
     return dict(loss=loss, dX=dX, dW=dW, L=L, row_loss=row_loss, z=z, s_x=s_x, s_g=s_g,
-                x8=x8, g8=g8, N=N)
+                x8=x8, g8=g8, N=N, z_exact=z_exact, g_scaled=g / s_g)
 
 
 # ---------------------------------------------------------------------------

@@ -13,11 +13,12 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsampledce.so")
 
-SCE_F32, SCE_BF16 = 0, 1
-DEV_TOO_MANY_TARGETS, DEV_LABEL_RANGE = 1, 2
+SCE_F32, SCE_BF16, SCE_E4M3 = 0, 1, 2
+DEV_TOO_MANY_TARGETS, DEV_LABEL_RANGE, DEV_SCALE_RANGE = 1, 2, 4
 STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
 
 EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sampled_ce_forward_backward",
+           "sampled_ce_forward_backward_fp8",
            "sce_ce_rows_workspace_size", "sce_ce_rows", "sce_gather_rows",
            "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
 STAGES = ("candidates", "logits", "ce", "dx", "dx_reduce", "dw", "scatter")
@@ -49,6 +50,10 @@ def load_library(path: str = LIB_PATH):
     lib.sampled_ce_forward_backward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                                 p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.sampled_ce_forward_backward.restype = i32
+    lib.sampled_ce_forward_backward_fp8.argtypes = [p, p, ctypes.c_float, p, p, i64, i64, i64, i64,
+                                                    i64, i64, p, p, p, p, p, p, p, p, p, p, p,
+                                                    sz, p]
+    lib.sampled_ce_forward_backward_fp8.restype = i32
     lib.sce_ce_rows_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
     lib.sce_ce_rows_workspace_size.restype = i32
     lib.sce_ce_rows.argtypes = [p, i64, i64, i64, i32, p, p, p, p, p, p, p, sz, p]
@@ -180,6 +185,64 @@ def forward_backward(x, W, targets, prefix_targets, P, stride, offset, *, output
         _ptr(ws), ws.numel(), _stream(dev))
     if rc != 0:
         raise SceError("sampled_ce_forward_backward", rc)
+    if o["C"] is not None:
+        o["C"] = o["C"][:P]
+    o["target_pos"] = o["target_pos"][:T]
+    o["prefix_pos"] = o["prefix_pos"][:T]
+    return o
+
+
+def forward_backward_fp8(x, W8, w_scale, targets, prefix_targets, P, stride, offset, *,
+                         outputs=None, ws=None, want_rows=False):
+    """One sampled-CE step with e4m3 product operands. x [T,d] bf16, W8 [V,d] the lm_head
+    as e4m3 codes (torch.uint8 or torch.float8_e4m3fn), w_scale its float dequantisation
+    scale, labels as in forward_backward.
+
+    Returns the keys of forward_backward (dX and dW bf16) plus `scales` (fp32 [2]:
+    s_x, s_g).
+    """
+    lib = load_library()
+    dev = x.device
+    T, d = x.shape
+    V = W8.shape[0]
+    if x.dtype != torch.bfloat16 or W8.shape[1] != d or W8.element_size() != 1:
+        raise ValueError("x must be bf16 and W8 one byte per element with x's hidden size")
+    for name, t in (("x", x), ("W8", W8), ("targets", targets)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if targets.dtype != torch.int64 or (prefix_targets is not None and prefix_targets.dtype != torch.int64):
+        raise ValueError("labels must be int64")
+    o = dict(outputs or {})
+    if "loss" not in o:
+        o["loss"] = torch.empty(1, dtype=torch.float32, device=dev)
+    if "dX" not in o:
+        o["dX"] = torch.empty_like(x)
+    if "dW" not in o:
+        o["dW"] = torch.empty(V, d, dtype=torch.bfloat16, device=dev)
+    if "C" not in o:
+        o["C"] = torch.empty(max(P, 1), dtype=torch.int32, device=dev) if P > 0 else None
+    for k in ("target_pos", "prefix_pos"):
+        if k not in o:
+            o[k] = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    if "aux" not in o:
+        o["aux"] = torch.empty(4, dtype=torch.int64, device=dev)
+    if "scales" not in o:
+        o["scales"] = torch.empty(2, dtype=torch.float32, device=dev)
+    if want_rows:
+        for k in ("row_lse", "row_loss"):
+            if k not in o:
+                o[k] = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+    nbytes = workspace_size(T, d, V, P, SCE_E4M3)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    rc = lib.sampled_ce_forward_backward_fp8(
+        _ptr(x), _ptr(W8), ctypes.c_float(w_scale), _ptr(targets), _ptr(prefix_targets), T, d, V,
+        P, stride, offset, _ptr(o["loss"]), _ptr(o["dX"]), _ptr(o["dW"]), _ptr(o["C"]),
+        _ptr(o["target_pos"]), _ptr(o["prefix_pos"]), _ptr(o.get("row_lse")),
+        _ptr(o.get("row_loss")), _ptr(o["aux"]), _ptr(o["scales"]), _ptr(ws), ws.numel(),
+        _stream(dev))
+    if rc != 0:
+        raise SceError("sampled_ce_forward_backward_fp8", rc)
     if o["C"] is not None:
         o["C"] = o["C"][:P]
     o["target_pos"] = o["target_pos"][:T]

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsampledce.so")
-SOURCES = ["api.hip", "candidates.hip", "gather_scatter.hip", "ce.hip", "gemm.hip", "gemm_bf16.hip"]
+SOURCES = ["api.hip", "candidates.hip", "gather_scatter.hip", "ce.hip", "gemm.hip", "gemm_bf16.hip",
+           "quant.hip"]
 ARCH = os.environ.get("SCE_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -32,18 +32,25 @@ int64_t mod64(int64_t a, int64_t m) {
 struct Plan {
   int64_t Peff = 0, ldz = 0;
   int64_t ldwc = 0;   // row pitch of the gathered W_C (elements)
+  int64_t ldg = 0;    // e4m3 step: row pitch of the e4m3 gradient (bytes)
   int splits = 1;     // k-split of the dW product (fp32 partials reduced by the scatter)
   int dx_splits = 1;  // k-split of the dX product (fp32 partials reduced into dX)
   size_t counters = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
   size_t wc = 0, z = 0, part = 0, total = 0;
+  size_t x8 = 0, g8 = 0, scales = 0;  // e4m3 step
 };
 
 // full = false: only what the candidate build needs.
 Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full) {
   Plan p;
-  const size_t es = dtype == SCE_BF16 ? 2 : 4;
+  const bool e4m3 = dtype == SCE_E4M3;
+  const size_t es = dtype == SCE_BF16 ? 2 : 4;  // logits element; the e4m3 step's are bf16
+  const size_t ws = e4m3 ? 1 : es;              // W_C element
   p.Peff = P == 0 ? V : P;
-  p.ldz = round_up(p.Peff, 8);
+  // e4m3 step: the gradient's rows share this pitch (a multiple of 16 bytes), and the
+  // cross-entropy writes every column below it (zeros past P), so a product's 16-element
+  // chunks that straddle K read zeros.
+  p.ldz = round_up(p.Peff, dtype == SCE_E4M3 ? 16 : 8);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -60,9 +67,16 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     // W_C rows are padded by 64 elements: with d * es a multiple of 512 bytes (d = 768
     // bf16: 1536 B), the logits product measured 15% slower on unpadded rows.
     p.ldwc = P > 0 ? d + 64 : d;
-    p.wc = take(P > 0 ? (size_t)P * p.ldwc * es : 0);
-    p.z = take((size_t)T * p.ldz * es);
-    if (dtype == SCE_BF16) {
+    p.wc = take(P > 0 ? (size_t)P * p.ldwc * ws : 0);
+    p.z = take((size_t)T * p.ldz * (e4m3 ? 2 : es));
+    if (e4m3) {
+      p.ldg = p.ldz;
+      p.x8 = take((size_t)T * d);
+      p.g8 = take((size_t)T * p.ldg);
+      p.scales = take(kNumScales * sizeof(float));
+      p.splits = gemm_fp8_dw_splits(p.Peff, d, T);
+      p.dx_splits = gemm_fp8_dx_splits(T, d, p.Peff);
+    } else if (dtype == SCE_BF16) {
       p.splits = gemm_bf16_dw_splits(p.Peff, d, T);
       p.dx_splits = gemm_bf16_dx_splits(T, d, p.Peff);
     } else {
@@ -87,7 +101,8 @@ sce_status check_sizes(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bo
   if (P > 0 && V > SCE_MAX_V_SAMPLED) return SCE_EINVAL;
   if (need_d && (d < 8 || d % 8 != 0 || d > SCE_MAX_D)) return SCE_EINVAL;
   if (need_d && T * d > SCE_MAX_TD) return SCE_EINVAL;
-  if (dtype != SCE_F32 && dtype != SCE_BF16) return SCE_EINVAL;
+  if (dtype != SCE_F32 && dtype != SCE_BF16 && dtype != SCE_E4M3) return SCE_EINVAL;
+  if (dtype == SCE_E4M3 && need_d && d % 16 != 0) return SCE_EINVAL;
   return SCE_OK;
 }
 
@@ -183,6 +198,7 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
                                        int32_t* prefix_pos_out, float* row_lse_out,
                                        float* row_loss_out, int64_t* aux_out, void* workspace,
                                        size_t workspace_bytes, void* stream) {
+  if (dtype == SCE_E4M3) return SCE_EINVAL;  // sampled_ce_forward_backward_fp8
   sce_status st = check_sizes(T, d, V, P, dtype, true);
   if (st != SCE_OK) return st;
   if (W == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
@@ -251,6 +267,93 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
     const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
     e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? vocab_pos : nullptr,
                             P > 0 ? cand : nullptr, (int)p.Peff, (int)V, (int)d, bf16, dW, &fin, hs);
+  }
+  marks.mark(SCE_NUM_STAGES);
+  return hip_status(e);
+}
+
+sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float w_scale,
+                                           const int64_t* targets, const int64_t* prefix_targets,
+                                           int64_t T, int64_t d, int64_t V, int64_t P,
+                                           int64_t stride, int64_t offset, float* loss, void* dX,
+                                           void* dW, int32_t* candidates_out,
+                                           int32_t* target_pos_out, int32_t* prefix_pos_out,
+                                           float* row_lse_out, float* row_loss_out,
+                                           int64_t* aux_out, float* scales_out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  sce_status st = check_sizes(T, d, V, P, SCE_E4M3, true);
+  if (st != SCE_OK) return st;
+  if (!(w_scale > 0.f) || w_scale > 3.0e38f) return SCE_EINVAL;  // also rejects NaN
+  if (W8 == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
+  if (T > 0 && (x == nullptr || targets == nullptr || dX == nullptr)) return SCE_EINVAL;
+  if ((x && !aligned16(x)) || !aligned16(W8) || (dX && !aligned16(dX)) || !aligned16(dW))
+    return SCE_EINVAL;
+  int64_t s = 1;
+  if (P > 0) {
+    s = mod64(stride, V);
+    if (gcd64(s, V) != 1) return SCE_EINVAL;
+  }
+  const Plan p = make_plan(T, d, V, P, SCE_E4M3, true);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  int32_t* vocab_pos = reinterpret_cast<int32_t*>(ws + p.vocab_pos);
+  int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
+  int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+  float* scales = reinterpret_cast<float*>(ws + p.scales);
+  void* Z = ws + p.z;
+  uint8_t* x8 = reinterpret_cast<uint8_t*>(ws + p.x8);
+  uint8_t* g8 = reinterpret_cast<uint8_t*>(ws + p.g8);
+  float* part = reinterpret_cast<float*>(ws + p.part);
+  const void* WC = P > 0 ? static_cast<const void*>(ws + p.wc) : W8;
+
+  StageMarks marks(hs);
+  marks.mark(SCE_STAGE_CANDIDATES);
+  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
+                                   (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
+                                   W8, (int)d, ws + p.wc, (int)p.ldwc, hs);
+  if (e == hipSuccess) e = launch_quant_x(x, T * d, counters, w_scale, x8, scales, scales_out, hs);
+  marks.mark(SCE_STAGE_LOGITS);
+  if (e == hipSuccess && T > 0) {
+    GemmArgs g{x8, d, WC, p.ldwc, Z, p.ldz, T, p.Peff, d, 1, 0, scales + kScaleLogits};
+    e = launch_gemm_fp8(Gemm::Logits, g, hs);
+  }
+  marks.mark(SCE_STAGE_CE);
+  if (e == hipSuccess) {
+    const G8Out go{g8, p.ldg, prefix_targets ? 2 : 1, scales, scales_out};
+    e = launch_ce_rows_g8(Z, p.ldz, (int)T, (int)p.Peff, tpos, ppos, counters, row_loss,
+                          row_lse_out, go, hs);
+  }
+  marks.mark(SCE_STAGE_DX);
+  if (e == hipSuccess && T > 0) {
+    if (p.dx_splits > 1) {
+      GemmArgs g{g8, p.ldg, WC, p.ldwc, part, d, T, d, p.Peff, p.dx_splits, T * d, scales + kScaleDx};
+      e = launch_gemm_fp8(Gemm::DX, g, hs);
+    } else {
+      GemmArgs g{g8, p.ldg, WC, p.ldwc, dX, d, T, d, p.Peff, 1, 0, scales + kScaleDx};
+      e = launch_gemm_fp8(Gemm::DX, g, hs);
+    }
+  }
+  marks.mark(SCE_STAGE_DX_REDUCE);
+  if (e == hipSuccess && T > 0 && p.dx_splits > 1)
+    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, nullptr, (int)T, (int)T, (int)d,
+                            true, dX, nullptr, hs);
+  marks.mark(SCE_STAGE_DW);
+  if (e == hipSuccess && T > 0) {
+    GemmArgs g{g8, p.ldg, x8, d, part, d, p.Peff, d, T, p.splits, p.Peff * d, scales + kScaleDw};
+    e = launch_gemm_fp8(Gemm::DW, g, hs);
+  }
+  marks.mark(SCE_STAGE_SCATTER);
+  if (e == hipSuccess) {
+    const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
+    // T = 0: no product ran; the scatter's zero blocks still clear every row of dW.
+    e = launch_scatter_rows(part, T > 0 ? p.splits : 0, p.Peff * d, P > 0 ? vocab_pos : nullptr,
+                            P > 0 ? cand : nullptr, (int)p.Peff, (int)V, (int)d, true, dW, &fin, hs);
   }
   marks.mark(SCE_NUM_STAGES);
   return hip_status(e);

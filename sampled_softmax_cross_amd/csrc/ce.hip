@@ -61,6 +61,35 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2)
   m = M;
 }
 
+// e4m3 output: 1 / s_g, where s_g is the smallest power of two with n_max / N <= 448 s_g,
+// i.e. 2^-k for the largest k with n_max 2^k <= 448 N. Every |g| <= n_t / N <= n_max / N,
+// so g / s_g stays within e4m3's largest finite value (448).
+__device__ __forceinline__ float grad_inv_scale(int N, int n_max) {
+  if (N <= 0) return 1.f;
+  const unsigned long long q = 448ull * (unsigned)N / (unsigned)n_max;
+  const int k = 63 - __clzll(q);
+  return __int_as_float((127 + k) << 23);
+}
+
+// Row 0 completes the scale table once s_g is known.
+__device__ __forceinline__ void write_grad_scales(const G8Out& go, float ginv) {
+  const float sg = 1.0f / ginv;  // exact: a power of two
+  go.scales[kScaleG] = sg;
+  go.scales[kScaleDx] = sg * go.scales[kScaleW];
+  go.scales[kScaleDw] = sg * go.scales[kScaleX];
+  if (go.scales_out) go.scales_out[1] = sg;
+}
+
+// Eight gradient values (already divided by s_g) as e4m3 codes (round to nearest even).
+__device__ __forceinline__ void store_g8(const G8Out& go, int t, int i, const float* g) {
+  uint2 o;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(g[0], g[1], 0, false);
+  o.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(g[2], g[3], w, true);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(g[4], g[5], 0, false);
+  o.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(g[6], g[7], w, true);
+  *reinterpret_cast<uint2*>(go.g8 + (int64_t)t * go.ldg + (int64_t)i * 8) = o;
+}
+
 // Block-wide merge; every thread gets the row's (max, sum). Contains barriers.
 template <int NT>
 __device__ __forceinline__ void block_merge_ms(float& m, float& s, float* red) {
@@ -93,16 +122,18 @@ __device__ __forceinline__ void opaque(uint4 (&q)[VPT]) {
   for (int k = 0; k < VPT; ++k) asm volatile("" : "+v"(q[k].x), "+v"(q[k].y), "+v"(q[k].z), "+v"(q[k].w));
 }
 
-// Register-resident row: NT lanes x VPT vectors of 16 bytes cover the row.
-template <typename TZ, int NT, int VPT>
+// Register-resident row: NT lanes x VPT vectors of 16 bytes cover the row. G8: the
+// gradient goes out as e4m3 codes of g / s_g (go), Z is only read.
+template <typename TZ, int NT, int VPT, bool G8>
 __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz, int P,
                                                 const int32_t* __restrict__ tpos,
                                                 const int32_t* __restrict__ ppos,
                                                 const int32_t* __restrict__ counters,
                                                 float* __restrict__ row_loss,
-                                                float* __restrict__ row_lse) {
+                                                float* __restrict__ row_lse, G8Out go) {
   using RV = RowVec<TZ>;
   constexpr int E = RV::kElems;
+  static_assert(!G8 || E == 8, "e4m3 output from bf16 rows");
   __shared__ float red[2 * (NT / kWave)];
   __shared__ float zlab[2];
   const int t = blockIdx.x;
@@ -193,7 +224,10 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
   const float L = M + __builtin_amdgcn_logf(S) * kLn2;  // logf here is log2
 
   const int N = counters[kNumLabels];
-  const float inv = N > 0 ? 1.0f / (float)N : 0.f;
+  const float ginv = G8 ? grad_inv_scale(N, go.n_max) : 1.f;
+  if constexpr (G8)
+    if (t == 0 && threadIdx.x == 0) write_grad_scales(go, ginv);
+  const float inv = N > 0 ? 1.0f / (float)N * ginv : 0.f;  // ginv: exact power of two
   const int nt = (tp >= 0) + (pp >= 0);
   // kKeep: exp(Z - L) = exp(Z - m_lane) * exp(m_lane - L); else exp(Z - L) directly.
   const float scale = kKeep ? (m == -INFINITY ? 0.f : (float)nt * inv * __builtin_amdgcn_exp2f((m - L) * kLog2e))
@@ -227,7 +261,8 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
           g[e] -= (float)((j == tp) + (j == pp)) * inv;
         }
       }
-      rowv[i] = RV::pack(g);
+      if constexpr (G8) store_g8(go, t, i, g);
+      else rowv[i] = RV::pack(g);
     }
   }
   if (threadIdx.x == 0) {
@@ -242,15 +277,16 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
 // Short rows (at most 64 * VPT vectors): one wave per row, four rows per workgroup,
 // the (max, sum) merge by shuffles only (no LDS, no barrier). The same arithmetic as
 // k_ce_rows with exp(Z - m_lane) kept per element.
-template <typename TZ, int VPT>
+template <typename TZ, int VPT, bool G8>
 __global__ __launch_bounds__(256) void k_ce_rows_wave(TZ* __restrict__ Z, int64_t ldz, int P,
                                                       int T, const int32_t* __restrict__ tpos,
                                                       const int32_t* __restrict__ ppos,
                                                       const int32_t* __restrict__ counters,
                                                       float* __restrict__ row_loss,
-                                                      float* __restrict__ row_lse) {
+                                                      float* __restrict__ row_lse, G8Out go) {
   using RV = RowVec<TZ>;
   constexpr int E = RV::kElems;
+  static_assert(!G8 || E == 8, "e4m3 output from bf16 rows");
   const int lane = threadIdx.x & (kWave - 1);
   const int t = (int)blockIdx.x * 4 + (int)(threadIdx.x / kWave);
   if (t >= T) return;  // a whole wave
@@ -297,7 +333,10 @@ __global__ __launch_bounds__(256) void k_ce_rows_wave(TZ* __restrict__ Z, int64_
   }
   const float L = M + __builtin_amdgcn_logf(S) * kLn2;  // logf here is log2
   const int N = counters[kNumLabels];
-  const float inv = N > 0 ? 1.0f / (float)N : 0.f;
+  const float ginv = G8 ? grad_inv_scale(N, go.n_max) : 1.f;
+  if constexpr (G8)
+    if (t == 0 && lane == 0) write_grad_scales(go, ginv);
+  const float inv = N > 0 ? 1.0f / (float)N * ginv : 0.f;  // ginv: exact power of two
   const int nt = (tp >= 0) + (pp >= 0);
   const float scale = m == -INFINITY ? 0.f
                                      : (float)nt * inv * __builtin_amdgcn_exp2f((m - L) * kLog2e);
@@ -317,7 +356,8 @@ __global__ __launch_bounds__(256) void k_ce_rows_wave(TZ* __restrict__ Z, int64_
           g[e] -= (float)((j == tp) + (j == pp)) * inv;
         }
       }
-      rowv[i] = RV::pack(g);
+      if constexpr (G8) store_g8(go, t, i, g);
+      else rowv[i] = RV::pack(g);
     }
   }
   if (lane == 0) {
@@ -330,15 +370,16 @@ __global__ __launch_bounds__(256) void k_ce_rows_wave(TZ* __restrict__ Z, int64_
 }
 
 // Rows too long for registers: two sweeps over HBM (online (max, sum), then write).
-template <typename TZ, int NT>
+template <typename TZ, int NT, bool G8>
 __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64_t ldz, int P,
                                                        const int32_t* __restrict__ tpos,
                                                        const int32_t* __restrict__ ppos,
                                                        const int32_t* __restrict__ counters,
                                                        float* __restrict__ row_loss,
-                                                       float* __restrict__ row_lse) {
+                                                       float* __restrict__ row_lse, G8Out go) {
   using RV = RowVec<TZ>;
   constexpr int E = RV::kElems;
+  static_assert(!G8 || E == 8, "e4m3 output from bf16 rows");
   __shared__ float red[2 * (NT / kWave)];
   __shared__ float zlab[2];
   const int t = blockIdx.x;
@@ -370,7 +411,10 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
   block_merge_ms<NT>(m, s, red);
   const float L = m + __builtin_amdgcn_logf(s) * kLn2;
   const int N = counters[kNumLabels];
-  const float inv = N > 0 ? 1.0f / (float)N : 0.f;
+  const float ginv = G8 ? grad_inv_scale(N, go.n_max) : 1.f;
+  if constexpr (G8)
+    if (t == 0 && threadIdx.x == 0) write_grad_scales(go, ginv);
+  const float inv = N > 0 ? 1.0f / (float)N * ginv : 0.f;  // ginv: exact power of two
   const float c = (float)((tp >= 0) + (pp >= 0)) * inv;
   __syncthreads();  // zlab was read before any lane writes the row
   for (int i = threadIdx.x; i < nvec; i += NT) {
@@ -383,7 +427,8 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
                          (float)((j == tp) + (j == pp)) * inv
                    : 0.f;
     }
-    rowv[i] = RV::pack(f);
+    if constexpr (G8) store_g8(go, t, i, f);
+    else rowv[i] = RV::pack(f);
   }
   if (threadIdx.x == 0) {
     float l = 0.f;
@@ -394,24 +439,21 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
   }
 }
 
-template <typename TZ, int NT, int VPT>
+template <typename TZ, int NT, int VPT, bool G8>
 static void launch_ce_fixed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp, const int32_t* pp,
-                            int32_t* counters, float* rl, float* lse, float* loss, int64_t* aux,
-                            hipStream_t s) {
-  (void)loss;
-  (void)aux;
-  hipLaunchKernelGGL((k_ce_rows<TZ, NT, VPT>), dim3(T), dim3(NT), 0, s, Z, ldz, P, tp, pp,
-                     counters, rl, lse);
+                            int32_t* counters, float* rl, float* lse, const G8Out& go, hipStream_t s) {
+  hipLaunchKernelGGL((k_ce_rows<TZ, NT, VPT, G8>), dim3(T), dim3(NT), 0, s, Z, ldz, P, tp, pp,
+                     counters, rl, lse, go);
 }
 
-template <typename TZ, int NT>
+template <typename TZ, int NT, bool G8>
 static bool launch_ce_nt(int vpt, TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
-                         const int32_t* pp, int32_t* counters, float* rl, float* lse, float* loss,
-                         int64_t* aux, hipStream_t s) {
+                         const int32_t* pp, int32_t* counters, float* rl, float* lse,
+                         const G8Out& go, hipStream_t s) {
   switch (vpt) {
 #define SCE_CE_CASE(n) \
   case n:              \
-    launch_ce_fixed<TZ, NT, n>(Z, ldz, T, P, tp, pp, counters, rl, lse, loss, aux, s); \
+    launch_ce_fixed<TZ, NT, n, G8>(Z, ldz, T, P, tp, pp, counters, rl, lse, go, s); \
     return true;
     SCE_CE_CASE(1) SCE_CE_CASE(2) SCE_CE_CASE(3) SCE_CE_CASE(4) SCE_CE_CASE(5) SCE_CE_CASE(6)
     SCE_CE_CASE(7) SCE_CE_CASE(8) SCE_CE_CASE(9) SCE_CE_CASE(10) SCE_CE_CASE(11) SCE_CE_CASE(12)
@@ -422,32 +464,32 @@ static bool launch_ce_nt(int vpt, TZ* Z, int64_t ldz, int T, int P, const int32_
   }
 }
 
-template <typename TZ>
+template <typename TZ, bool G8>
 static void launch_ce_typed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
                             const int32_t* pp, int32_t* counters, float* rl, float* lse,
-                            float* loss, int64_t* aux, hipStream_t s) {
+                            const G8Out& go, hipStream_t s) {
   constexpr int E = RowVec<TZ>::kElems;
   const int64_t nvec = ldz / E;
   if (nvec <= kWave * 4) {
     const int vpt = (int)((nvec + kWave - 1) / kWave);
     const dim3 grid((T + 3) / 4), block(256);
     if (vpt <= 1)
-      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 1>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 1, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
     else if (vpt == 2)
-      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 2>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 2, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
     else if (vpt == 3)
-      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 3>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 3, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
     else
-      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 4>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse);
+      hipLaunchKernelGGL((k_ce_rows_wave<TZ, 4, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
   } else if (nvec <= 256 * 16) {
-    launch_ce_nt<TZ, 256>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse,
-                          loss, aux, s);
+    launch_ce_nt<TZ, 256, G8>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse,
+                              go, s);
   } else if (nvec <= 512 * 16) {
-    launch_ce_nt<TZ, 512>((int)((nvec + 511) / 512), Z, ldz, T, P, tp, pp, counters, rl, lse,
-                          loss, aux, s);
+    launch_ce_nt<TZ, 512, G8>((int)((nvec + 511) / 512), Z, ldz, T, P, tp, pp, counters, rl, lse,
+                              go, s);
   } else {
-    hipLaunchKernelGGL((k_ce_rows_stream<TZ, 1024>), dim3(T), dim3(1024), 0, s, Z, ldz, P, tp,
-                       pp, counters, rl, lse);
+    hipLaunchKernelGGL((k_ce_rows_stream<TZ, 1024, G8>), dim3(T), dim3(1024), 0, s, Z, ldz, P, tp,
+                       pp, counters, rl, lse, go);
   }
 }
 
@@ -498,12 +540,22 @@ hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
                           const int32_t* counters, float* row_loss, float* row_lse,
                           hipStream_t s) {
   if (T <= 0) return hipGetLastError();
+  const G8Out none{};
   if (bf16)
-    launch_ce_typed<bf16_t>(static_cast<bf16_t*>(Z), ldz, T, P, target_pos, prefix_pos,
-                            const_cast<int32_t*>(counters), row_loss, row_lse, nullptr, nullptr, s);
+    launch_ce_typed<bf16_t, false>(static_cast<bf16_t*>(Z), ldz, T, P, target_pos, prefix_pos,
+                                   const_cast<int32_t*>(counters), row_loss, row_lse, none, s);
   else
-    launch_ce_typed<float>(static_cast<float*>(Z), ldz, T, P, target_pos, prefix_pos,
-                           const_cast<int32_t*>(counters), row_loss, row_lse, nullptr, nullptr, s);
+    launch_ce_typed<float, false>(static_cast<float*>(Z), ldz, T, P, target_pos, prefix_pos,
+                                  const_cast<int32_t*>(counters), row_loss, row_lse, none, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_rows_g8(const void* Z, int64_t ldz, int T, int P, const int32_t* target_pos,
+                             const int32_t* prefix_pos, const int32_t* counters, float* row_loss,
+                             float* row_lse, const G8Out& go, hipStream_t s) {
+  if (T <= 0) return hipGetLastError();
+  launch_ce_typed<bf16_t, true>(static_cast<bf16_t*>(const_cast<void*>(Z)), ldz, T, P, target_pos,
+                                prefix_pos, const_cast<int32_t*>(counters), row_loss, row_lse, go, s);
   return hipGetLastError();
 }
 

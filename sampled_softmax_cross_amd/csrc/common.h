@@ -15,10 +15,24 @@ enum Counter : int {
   kDistinct = 2,   // distinct targets
   kNextOffset = 3, // sweep offset after the build
   kCeDone = 4,     // CE rows finished (the last one reduces the loss)
+  kAmaxX = 5,      // e4m3 step: bf16 magnitude bits of max|x|
   kNumCounters = 8
 };
 constexpr int kDevTooManyTargets = 1;
 constexpr int kDevLabelRange = 2;
+constexpr int kDevScaleRange = 4;
+
+// e4m3 step: the scale table in the workspace (floats). The three products' output
+// factors, and the per-tensor scales they are made of.
+enum Scale : int {
+  kScaleLogits = 0,  // s_x * w_scale
+  kScaleDx = 1,      // s_g * w_scale
+  kScaleDw = 2,      // s_g * s_x
+  kScaleX = 3,       // s_x
+  kScaleG = 4,       // s_g
+  kScaleW = 5,       // w_scale
+  kNumScales = 8
+};
 
 // bfloat16 is carried as its 16 raw bits.
 using bf16_t = uint16_t;

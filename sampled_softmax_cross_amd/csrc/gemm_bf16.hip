@@ -1,34 +1,58 @@
-// Multi-stage bf16 MFMA GEMM for gfx950 (the logits, dX and dW products of the step).
+// Multi-stage MFMA GEMM for gfx950 (the logits, dX and dW products of the step), for
+// bf16 operands (EB = 2 bytes per element) and OCP e4m3 operands (EB = 1).
 //
 // Every operand tile travels global -> LDS by buffer_load ... lds (no VGPR staging,
-// no ds_write), through an NS-deep ring of LDS stages of SK k each (32 or 64), so a
-// tile is requested NS-1 stage-times before the MFMAs need it and the load latency of
-// a busy memory system stays hidden behind the matrix cores.
+// no ds_write), through an NS-deep ring of LDS stages of SK k each, so a tile is
+// requested NS-1 stage-times before the MFMAs need it and the load latency of a busy
+// memory system stays hidden behind the matrix cores.
 //
-// Operand layouts in LDS:
+// Operand layouts in LDS (16-byte chunks):
 //  * r-major (element (r, k) at P[r * ld + k], k contiguous): rows of SK k (64 or
-//    128 B), the 16-byte chunks of a row XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3
-//    (SK = 32) or (row >> 1) & 7 (SK = 64); a fragment (8 consecutive k of one row) is
-//    one ds_read_b128. With SK = 64 every row of a stage is one whole 128-byte line of
-//    the operand, which halves the cache requests per byte against SK = 32.
+//    128 B), the chunks of a row XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3 (64-byte
+//    rows) or (row >> 1) & 7 (128-byte rows). A lane's fragment is 16 (bf16) or 32
+//    (e4m3) consecutive bytes of one row: one or two ds_read_b128. With 128-byte rows
+//    every row of a stage is one whole line of the operand, which halves the cache
+//    requests per byte against 64-byte rows.
 //  * k-major (element (r, k) at P[k * ld + r]): the tile is kept as it is in memory,
-//    SK rows of k, each R elements wide, 16-byte chunks XOR-swizzled by 4 * (k & 3)
-//    (R a multiple of 128) or 4 * ((k >> 1) & 1) (R = 192).
-//    Fragments are read with ds_read_b64_tr_b16: within each 16-lane group, lane j
-//    receives element i from the address supplied by lane 4i + j/4 (at element
-//    offset j % 4), so lanes that point at rows k..k+3 and 4-column groups assemble
-//    8-k fragments of single columns without any transpose pass.
-// Both swizzles spread a fragment read over all LDS banks; the DMA fill picks, for
-// each lane, the global chunk that belongs at its (linear) LDS position.
+//    SK rows of k, each R elements wide. bf16: chunks XOR-swizzled by 4 * (k & 3) (rows
+//    of a multiple of 256 bytes) or 4 * ((k >> 1) & 1) (384-byte rows); fragments are
+//    read with ds_read_b64_tr_b16: within each 16-lane group, lane j receives element i
+//    from the address supplied by lane 4i + j/4 (at element offset j % 4), so lanes
+//    that point at rows k..k+3 and 4-column groups assemble 8-k fragments of single
+//    columns. e4m3: chunks XOR-swizzled by k & 7 (rows of a multiple of 128 bytes) or
+//    (k >> 1) & 3 (192-byte rows); ds_read_b64_tr_b8 gives lane j byte i from the
+//    address of lane 2i + j/8 (at byte offset j % 8): lanes pointing at rows k..k+7 and
+//    8-column groups assemble 8-k pieces of single columns, four of which make a
+//    32-k fragment.
+// The swizzles spread a fragment read over all LDS banks; the DMA fill picks, for each
+// lane, the global chunk that belongs at its (linear) LDS position.
 //
-// The MFMA (v_mfma_f32_32x32x16_bf16) takes the B-tile fragment first, which makes
-// every accumulator block the transposed output and lets the epilogue write 16-byte
-// vectors straight from registers (see store_acc).
+// The MFMA (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// scales for e4m3) takes the B-tile fragment first, which makes every accumulator
+// block the transposed output and lets the epilogue write 16-byte vectors straight
+// from registers (see store_acc). Lane l holds k = kgroup * (l / 32) + [0, kgroup) of
+// its row or column in both operands (8 for bf16, 32 for e4m3).
 #include "gemm_common.h"
 
 namespace sce {
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Per element size: the fragment a lane holds for one MFMA and the k one MFMA covers.
+template <int EB>
+struct MfmaElem;
+template <>
+struct MfmaElem<2> {
+  using frag_t = bf16x8_t;
+  static constexpr int kMfmaK = 16;
+};
+template <>
+struct MfmaElem<1> {
+  using frag_t = i32x8_t;
+  static constexpr int kMfmaK = 64;
+};
 
 // s_waitcnt vmcnt(n) with expcnt and lgkmcnt at their maxima (gfx9 encoding).
 template <int N>
@@ -37,36 +61,49 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// LDS chunk (16 B) holding chunk `ch` of r-major row `row` (SK / 8 chunks per row).
-template <int SK>
+// LDS chunk (16 B) holding chunk `ch` of r-major row `row` (CPR chunks per row).
+template <int CPR>
 __device__ __forceinline__ int rm_swizzle(int row) {
-  if constexpr (SK == 32) return ((row >> 1) ^ (row >> 3)) & 3;
+  if constexpr (CPR == 4) return ((row >> 1) ^ (row >> 3)) & 3;
   else return (row >> 1) & 7;
 }
-template <int SK>
+template <int CPR>
 __device__ __forceinline__ int rm_index(int row, int ch) {
-  return row * (SK / 8) + (ch ^ rm_swizzle<SK>(row));
+  return row * CPR + (ch ^ rm_swizzle<CPR>(row));
 }
-// k-major chunk swizzle: rows k..k+3 that one transposing read touches land on
-// distinct 64-byte bank groups. Rows of a multiple of 256 bytes (R % 128 == 0) start
-// on the same banks, so they shift by 4 * (k & 3) chunks; 384-byte rows (R = 192)
-// alternate between two bank offsets, so rows k and k + 2 shift by 4 chunks.
-template <int R>
+// k-major chunk swizzle for rows of RB bytes: the rows one transposing read touches
+// land on distinct bank groups. bf16 reads touch rows k..k+3 with 8 bytes each per
+// lane quad: rows of a multiple of 256 bytes start on the same banks, so they shift by
+// 4 * (k & 3) chunks; 384-byte rows alternate between two bank offsets, so rows k and
+// k + 2 shift by 4 chunks. e4m3 reads touch rows k..k+7, 16 bytes each: rows of a
+// multiple of 128 bytes shift by k & 7 chunks; 192-byte rows alternate between two
+// offsets 64 bytes apart, so rows k, k + 2, k + 4, k + 6 shift by (k >> 1) & 3.
+template <int RB, int EB>
 __device__ __forceinline__ int km_swizzle(int k) {
-  if constexpr (R % 128 == 0) return (k & 3) << 2;
-  else return ((k >> 1) & 1) << 2;
+  if constexpr (EB == 2) {
+    if constexpr (RB % 256 == 0) return (k & 3) << 2;
+    else return ((k >> 1) & 1) << 2;
+  } else {
+    if constexpr (RB % 128 == 0) return k & 7;
+    else return (k >> 1) & 3;
+  }
 }
-template <int R>
+template <int RB, int EB>
 __device__ __forceinline__ int km_index(int k, int ch) {
-  return k * (R / 8) + (ch ^ km_swizzle<R>(k));
+  return k * (RB / 16) + (ch ^ km_swizzle<RB, EB>(k));
 }
 
-// One operand tile of R rows (r-major) or R columns (k-major) by SK k per stage,
-// filled by NW waves (64 chunks of 16 B per instruction).
-template <int R, bool KMAJ, int NW, int SK>
+// One operand tile of R rows (r-major) or R columns (k-major) by SK k per stage of
+// EB-byte elements, filled by NW waves (64 chunks of 16 B per instruction).
+template <int R, bool KMAJ, int NW, int SK, int EB>
 struct DmaTile {
-  static_assert((R * SK) % (512 * NW) == 0 && (!KMAJ || R % 128 == 0 || R == 192), "tile shape");
-  static constexpr int kN = R * SK / (512 * NW);  // DMA instructions per wave per stage
+  static constexpr int CPR = SK * EB / 16;  // chunks per r-major row
+  static constexpr int RB = R * EB;         // bytes per k-major row
+  static constexpr int EPC = 16 / EB;       // elements per chunk
+  static_assert((R * SK * EB) % (1024 * NW) == 0 && (CPR == 4 || CPR == 8) &&
+                    (!KMAJ || RB % 256 == 0 || RB == 384 || (EB == 1 && (RB % 128 == 0 || RB == 192))),
+                "tile shape");
+  static constexpr int kN = R * SK * EB / (1024 * NW);  // DMA instructions per wave per stage
   int off[kN];  // byte offset of the lane's chunk from the tile origin
   int kr[kN];   // (k << 16) | row of the lane's chunk, for the clip: k of the chunk
                 // (r-major) or its row (k-major), and its row (r-major) or first column
@@ -79,19 +116,19 @@ struct DmaTile {
       const int q = 64 * (w * kN + i) + lane;  // linear LDS chunk this lane fills
       int r, k;
       if constexpr (!KMAJ) {
-        r = q / (SK / 8);
-        k = ((q % (SK / 8)) ^ rm_swizzle<SK>(r)) * 8;
+        r = q / CPR;
+        k = ((q % CPR) ^ rm_swizzle<CPR>(r)) * EPC;
       } else {
-        k = q / (R / 8);
-        r = ((q % (R / 8)) ^ km_swizzle<R>(k)) * 8;
+        k = q / (RB / 16);
+        r = ((q % (RB / 16)) ^ km_swizzle<RB, EB>(k)) * EPC;
       }
       kr[i] = (k << 16) | r;
-      off[i] = (int)((KMAJ ? (int64_t)k * ld + r : (int64_t)r * ld + k) * 2);
+      off[i] = (int)((KMAJ ? (int64_t)k * ld + r : (int64_t)r * ld + k) * EB);
     }
   }
   // base: address of tile element (0, 0) of this stage; rows_valid / k_valid clip the
   // tile (a clipped chunk reads zeros).
-  __device__ __forceinline__ void issue(const bf16_t* base, int64_t rows_valid, int64_t k_valid,
+  __device__ __forceinline__ void issue(const void* base, int64_t rows_valid, int64_t k_valid,
                                         uint4* tile) const {
     const rsrc_t rs = make_rsrc(base);
 #pragma unroll
@@ -102,29 +139,62 @@ struct DmaTile {
   }
 };
 
-// Fragment of 8 consecutive k (k-step ks of the stage) for tile row/column `r`
-// (this lane's own; r already includes lane % 32).
-template <int R, bool KMAJ, int SK>
-__device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int r_blk, int ks,
-                                              int lane) {
-  if constexpr (!KMAJ) {
-    return __builtin_bit_cast(bf16x8_t, tile[rm_index<SK>(r_lane, 2 * ks + (lane >> 5))]);
-  } else {
-    const int G = lane >> 4, a = lane & 15;
-    const int c = r_blk + 16 * (G & 1) + 4 * (a & 3);  // column this lane points at
-    const char* base = reinterpret_cast<const char*>(tile);
-    i16x4_t h[2];
+// This lane's fragment (k-step ks of the stage) for tile row/column `r_lane` (r_blk:
+// first row/column of its 32-block): 8 consecutive bf16 k or 32 consecutive e4m3 k.
+template <int R, bool KMAJ, int SK, int EB>
+__device__ __forceinline__ typename MfmaElem<EB>::frag_t read_frag(const uint4* tile, int r_lane,
+                                                               int r_blk, int ks, int lane) {
+  constexpr int CPR = SK * EB / 16, RB = R * EB;
+  const char* base = reinterpret_cast<const char*>(tile);
+  if constexpr (EB == 2) {
+    if constexpr (!KMAJ) {
+      return __builtin_bit_cast(bf16x8_t, tile[rm_index<CPR>(r_lane, 2 * ks + (lane >> 5))]);
+    } else {
+      const int G = lane >> 4, a = lane & 15;
+      const int c = r_blk + 16 * (G & 1) + 4 * (a & 3);  // column this lane points at
+      i16x4_t h[2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int k = 16 * ks + 8 * (G >> 1) + 4 * h2 + (a >> 2);
-      const int byte = km_index<R>(k, c >> 3) * 16 + (c & 7) * 2;
-      h[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(base + byte));
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int k = 16 * ks + 8 * (G >> 1) + 4 * h2 + (a >> 2);
+        const int byte = km_index<RB, EB>(k, c >> 3) * 16 + (c & 7) * 2;
+        h[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(base + byte));
+      }
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+      return __builtin_bit_cast(bf16x8_t, v);
     }
-    typedef short i16x8_t __attribute__((ext_vector_type(8)));
-    const i16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-    return __builtin_bit_cast(bf16x8_t, v);
+  } else {
+    if constexpr (!KMAJ) {
+      const int ch = 4 * ks + 2 * (lane >> 5);
+      const uint4 lo = tile[rm_index<CPR>(r_lane, ch)], hi = tile[rm_index<CPR>(r_lane, ch + 1)];
+      const i32x8_t v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      return v;
+    } else {
+      const int G = lane >> 4, a = lane & 15;
+      const int c = r_blk + 16 * (G & 1) + 8 * (a & 1);  // 8 columns this lane points at
+      i32x2_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = 64 * ks + 32 * (G >> 1) + 8 * q + (a >> 1);
+        const int byte = km_index<RB, EB>(k, c >> 4) * 16 + (c & 15);
+        h[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(base + byte));
+      }
+      const i32x8_t v = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+      return v;
+    }
   }
+}
+
+template <int EB>
+__device__ __forceinline__ void mfma(const typename MfmaElem<EB>::frag_t& b, const typename MfmaElem<EB>::frag_t& a,
+                                     f32x16_t& acc) {
+  if constexpr (EB == 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
+  else  // formats 0/0: both operands e4m3; E8M0 scales of 127 are 2^0
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, 0, 127, 0, 127);
 }
 
 // Persistent kernel: each workgroup takes the work units (output tile, k-split)
@@ -136,26 +206,31 @@ __device__ __forceinline__ bf16x8_t read_frag(const uint4* tile, int r_lane, int
 // streams from HBM can run further ahead than one that stays in the caches. IL: issue
 // the fragment reads one per MFMA (sched_group_barrier) instead of leaving the
 // interleave to the compiler; which is faster depends on the product (measured).
+// EB: bytes per operand element (2: bf16; 1: e4m3, whose products are multiplied by
+// *scale, a device value, before they are stored).
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
-          int SK, int NSB, bool IL>
-__global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
-    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ B, int64_t ldb,
+          int SK, int NSB, bool IL, int EB>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
+    const void* __restrict__ A, int64_t lda, const void* __restrict__ B, int64_t ldb,
     void* __restrict__ Cout, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t kps,
-    int64_t split_stride, int splits) {
+    int64_t split_stride, int splits, const float* __restrict__ scale) {
+  using frag_t = typename MfmaElem<EB>::frag_t;
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tiles are whole 32x32 MFMA blocks");
-  constexpr int A_SLOT = BM * SK / 8;  // uint4 per A stage
-  constexpr int B_SLOT = BN * SK / 8;  // uint4 per B stage
-  constexpr int LA = BM * SK / (512 * NW), LB = BN * SK / (512 * NW);  // DMA per wave
-  constexpr int KS = SK / 16;  // MFMA k-steps per stage
+  constexpr int A_SLOT = BM * SK * EB / 16;  // uint4 per A stage
+  constexpr int B_SLOT = BN * SK * EB / 16;  // uint4 per B stage
+  constexpr int LA = BM * SK * EB / (1024 * NW), LB = BN * SK * EB / (1024 * NW);  // DMA per wave
+  constexpr int KS = SK / MfmaElem<EB>::kMfmaK;  // MFMA k-steps per stage
   // Each step issues A then B (equal depths) or B then A (B shallower). Waiting for
   // stage g + 1 leaves in flight what was issued after its later half: whole steps,
   // plus one A group when B runs shallower.
   constexpr int WAIT = NSB < NS ? LA + (NSB - 2) * (LA + LB) : (NS - 2) * (LA + LB);
   constexpr int WAIT0 = (NSB - 1) * LB + (NS - 1) * LA;  // prologue: stage 0 landed
-  static_assert((SK == 32 || SK == 64) && NSB >= 2 && NSB <= NS && WAIT0 < 64, "pipeline shape");
+  // KS even: the last k-step of a stage reads fragment buffer 1 while the next stage's
+  // first fragments go to buffer 0.
+  static_assert(KS >= 2 && KS % 2 == 0 && NSB >= 2 && NSB <= NS && WAIT0 < 64, "pipeline shape");
   // Equal depths: stage s holds its A tile then its B tile (one slot of A_SLOT + B_SLOT);
   // otherwise an A ring followed by a B ring.
   __shared__ uint4 lds[NS * A_SLOT + NSB * B_SLOT];
@@ -189,8 +264,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     return c;
   };
 
-  DmaTile<BM, A_KM, NW, SK> ta;
-  DmaTile<BN, B_KM, NW, SK> tb;
+  DmaTile<BM, A_KM, NW, SK, EB> ta;
+  DmaTile<BN, B_KM, NW, SK, EB> tb;
+  const char* const Ab = static_cast<const char*>(A);
+  const char* const Bb = static_cast<const char*>(B);
   ta.init(lda, wid);
   tb.init(ldb, wid);
   // Issue cursors (unit iu, stage is of that unit), one per operand. Past the last unit,
@@ -212,14 +289,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   auto issue_a = [&](int slot_idx) {
     const int64_t k0 = ca.c.kb + (int64_t)ca.is * SK;
     const int64_t kv = ca.iu < my_units ? ca.c.ke - k0 : 0;
-    ta.issue(A_KM ? A + k0 * lda + ca.c.m0 : A + ca.c.m0 * lda + k0, M - ca.c.m0, kv,
+    ta.issue(Ab + (A_KM ? k0 * lda + ca.c.m0 : ca.c.m0 * lda + k0) * EB, M - ca.c.m0, kv,
              a_slot(slot_idx));
     advance(ca);
   };
   auto issue_b = [&](int slot_idx) {
     const int64_t k0 = cb.c.kb + (int64_t)cb.is * SK;
     const int64_t kv = cb.iu < my_units ? cb.c.ke - k0 : 0;
-    tb.issue(B_KM ? B + k0 * ldb + cb.c.n0 : B + cb.c.n0 * ldb + k0, N - cb.c.n0, kv,
+    tb.issue(Bb + (B_KM ? k0 * ldb + cb.c.n0 : cb.c.n0 * ldb + k0) * EB, N - cb.c.n0, kv,
              b_slot(slot_idx));
     advance(cb);
   };
@@ -229,9 +306,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   auto issue_stage = [&](int slot_idx) {
     const int64_t k0 = ca.c.kb + (int64_t)ca.is * SK;
     const int64_t kv = ca.iu < my_units ? ca.c.ke - k0 : 0;
-    ta.issue(A_KM ? A + k0 * lda + ca.c.m0 : A + ca.c.m0 * lda + k0, M - ca.c.m0, kv,
+    ta.issue(Ab + (A_KM ? k0 * lda + ca.c.m0 : ca.c.m0 * lda + k0) * EB, M - ca.c.m0, kv,
              a_slot(slot_idx));
-    tb.issue(B_KM ? B + k0 * ldb + ca.c.n0 : B + ca.c.n0 * ldb + k0, N - ca.c.n0, kv,
+    tb.issue(Bb + (B_KM ? k0 * ldb + ca.c.n0 : ca.c.n0 * ldb + k0) * EB, N - ca.c.n0, kv,
              b_slot(slot_idx));
     advance(ca);
   };
@@ -239,16 +316,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
   const int arow = wm * WM;  // wave's first row / column in the tile
   const int bcol = wn * WN;
   const int l32 = lane & 31;
-  bf16x8_t fa[2][TM], fb[2][TN];
+  frag_t fa[2][TM], fb[2][TN];
   auto read_frags = [&](int g, int ks, int buf) {
     const uint4* as = a_slot(g % NS);
     const uint4* bs = b_slot(g % NSB);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      fa[buf][i] = read_frag<BM, A_KM, SK>(as, arow + i * 32 + l32, arow + i * 32, ks, lane);
+      fa[buf][i] = read_frag<BM, A_KM, SK, EB>(as, arow + i * 32 + l32, arow + i * 32, ks, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      fb[buf][j] = read_frag<BN, B_KM, SK>(bs, bcol + j * 32 + l32, bcol + j * 32, ks, lane);
+      fb[buf][j] = read_frag<BN, B_KM, SK, EB>(bs, bcol + j * 32 + l32, bcol + j * 32, ks, lane);
   };
   f32x16_t acc[TM][TN];
   auto mfma_step = [&](int buf) {
@@ -256,9 +333,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+        mfma<EB>(fb[buf][j], fa[buf][i], acc[i][j]);
   };
-  constexpr int kReads = (A_KM ? 2 : 1) * TM + (B_KM ? 2 : 1) * TN;
+  // ds_read instructions per k-step: bf16 1 (r-major) or 2 (k-major) per fragment, e4m3 2 or 4
+  constexpr int kReads = (A_KM ? 2 : 1) * (3 - EB) * TM + (B_KM ? 2 : 1) * (3 - EB) * TN;
   constexpr int kMfma = TM * TN;
   auto interleave = [&]() {
     if constexpr (IL) {
@@ -322,25 +400,40 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_bf16(
       mfma_step((KS - 1) & 1);
       interleave();
     }
+    if constexpr (EB == 1) {
+      const float sc = *scale;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc;
+    }
     store_acc<OUT, TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow + l32, cc.n0 + bcol, lane >> 5,
                            OUT == kOutF32Split ? (cc.kb / kps) * split_stride : 0);
   }
 }
 
-#define SCE_GEMM16_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL)                 \
-  template __global__ void k_gemm_bf16<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL>( \
-      const bf16_t*, int64_t, const bf16_t*, int64_t, void*, int64_t, int64_t, int64_t, int64_t, \
-      int64_t, int64_t, int);
-SCE_GEMM16_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2, true)
-SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64, 2, false)
-SCE_GEMM16_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2, false)
-SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32, 3, true)
-SCE_GEMM16_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32, 3, true)
-SCE_GEMM16_INST(256, 256, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false)
-#undef SCE_GEMM16_INST
+#define SCE_GEMM_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL, EB)                 \
+  template __global__ void k_gemm_mfma<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL, EB>( \
+      const void*, int64_t, const void*, int64_t, void*, int64_t, int64_t, int64_t, int64_t,     \
+      int64_t, int64_t, int, const float*);
+SCE_GEMM_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2, true, 2)
+SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64, 2, false, 2)
+SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2, false, 2)
+SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32, 3, true, 2)
+SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32, 3, true, 2)
+SCE_GEMM_INST(256, 256, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false, 2)
+SCE_GEMM_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 128, 2, true, 1)
+SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 128, 2, false, 1)
+SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 128, 2, false, 1)
+SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutBF16, 2, 1, 128, 2, true, 1)
+SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutF32Split, 2, 1, 128, 2, true, 1)
+SCE_GEMM_INST(256, 256, 4, 2, true, true, kOutF32Split, 2, 1, 128, 2, false, 1)
+#undef SCE_GEMM_INST
 
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
-          int SK, int NSB, bool IL>
+          int SK, int NSB, bool IL, int EB = 2>
 static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   const int splits = a.splits > 0 ? a.splits : 1;
   int64_t kps = (a.K + splits - 1) / splits;
@@ -354,10 +447,10 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   // workgroup's units on one XCD), or one per unit when there are fewer.
   const int slots = cu_count() * OCC;
   const int grid = (int)(units < slots ? units : slots);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK, NSB, IL>),
-                     dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, s, static_cast<const bf16_t*>(a.A), a.lda,
-                     static_cast<const bf16_t*>(a.B), a.ldb, a.C, a.ldc, a.M, a.N, a.K, kps,
-                     a.split_stride, splits);
+  if (EB == 1 && a.scale == nullptr) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK, NSB, IL, EB>),
+                     dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, s, a.A, a.lda, a.B, a.ldb, a.C,
+                     a.ldc, a.M, a.N, a.K, kps, a.split_stride, splits, a.scale);
   return hipGetLastError();
 }
 
@@ -402,13 +495,14 @@ static int splits_for(int64_t M, int64_t N, int64_t K, int max_splits, bool spli
 
 // dW (M = P, N = d, K = T: few output tiles, long k): the k-split that minimises an
 // estimate of the product's time. Units run in whole rounds of one per CU, each round
-// streaming ceil(K / s) k at about 1.0 PFLOP/s over the chip (measured full-round rate of
-// this configuration); every split adds an fp32 partial of M x N that is written here
-// and read once by the reduction (8 bytes per element at about 5 TB/s).
-int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K) {
+// streaming ceil(K / s) k at the configuration's full-round rate over the chip (`flops`:
+// about 1.0 PFLOP/s measured for bf16; twice that assumed for e4m3, whose MFMA rate is
+// twice bf16's); every split adds an fp32 partial of M x N that is written here and read
+// once by the reduction (8 bytes per element at about 5 TB/s).
+static int gemm_dw_splits(int64_t M, int64_t N, int64_t K, double flops) {
   const int64_t tiles = ((M + kDwM - 1) / kDwM) * ((N + kDwN - 1) / kDwN);
   const int64_t slots = cu_count();
-  const double ns_per_k = 2.0 * kDwM * kDwN * (double)slots / 1.0e6;  // one round, 1e15 FLOP/s
+  const double ns_per_k = 2.0 * kDwM * kDwN * (double)slots / flops * 1.0e9;  // one round
   const double ns_per_partial = 8.0 * (double)M * (double)N / 5.0e3;  // 5e12 B/s
   int best = 1;
   double best_ns = 0.0;
@@ -423,10 +517,33 @@ int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K) {
   }
   return best;
 }
+int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K) { return gemm_dw_splits(M, N, K, 1.0e15); }
+int gemm_fp8_dw_splits(int64_t M, int64_t N, int64_t K) { return gemm_dw_splits(M, N, K, 2.0e15); }
 
 int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K) {
   return dx_wide(N) ? splits_for(M, N, K, 4, true, kWideM, kWideN, 1)
                     : splits_for(M, N, K, 4, true, kTileM, kTileN, kOcc);
+}
+
+hipError_t launch_gemm_fp8(Gemm kind, const GemmArgs& a, hipStream_t s) {
+  switch (kind) {
+    case Gemm::Logits: return run16<256, 256, 2, 4, false, false, kOutBF16, 2, 1, 128, 2, true, 1>(a, s);
+    case Gemm::DX:
+      if (dx_wide(a.N))
+        return a.splits > 1
+                   ? run16<kWideM, kWideN, 4, 2, false, true, kOutF32Split, 2, 1, 128, 2, false, 1>(a, s)
+                   : run16<kWideM, kWideN, 4, 2, false, true, kOutBF16, 2, 1, 128, 2, false, 1>(a, s);
+      return a.splits > 1
+                 ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 2, 1, 128, 2, true, 1>(a, s)
+                 : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 2, 1, 128, 2, true, 1>(a, s);
+    case Gemm::DW: return run16<kDwM, kDwN, 4, 2, true, true, kOutF32Split, 2, 1, 128, 2, false, 1>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int gemm_fp8_dx_splits(int64_t M, int64_t N, int64_t K) {
+  return dx_wide(N) ? splits_for(M, N, K, 4, true, kWideM, kWideN, 1)
+                    : splits_for(M, N, K, 4, true, kTileM, kTileN, 1);
 }
 
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {

@@ -79,6 +79,24 @@ hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
                           const int32_t* target_pos, const int32_t* prefix_pos,
                           const int32_t* counters, float* row_loss, float* row_lse,
                           hipStream_t s);
+// e4m3 step: the same over bf16 Z, with the gradient written as e4m3 codes of g / s_g
+// to its own buffer (Z is left as it is) and s_g derived from N.
+struct G8Out {
+  uint8_t* g8;        // [T, ldg] codes; columns [P, ldg) are not written
+  int64_t ldg;        // a multiple of 16, >= ldz
+  int n_max;          // labels per row at most: 1, or 2 with prefix targets
+  float* scales;      // the step's scale table (reads kScaleX, kScaleW; writes the rest)
+  float* scales_out;  // caller's {s_x, s_g}, or null (writes [1])
+};
+hipError_t launch_ce_rows_g8(const void* Z, int64_t ldz, int T, int P, const int32_t* target_pos,
+                             const int32_t* prefix_pos, const int32_t* counters, float* row_loss,
+                             float* row_lse, const G8Out& go, hipStream_t s);
+
+// e4m3 step: max|x| over bf16 x [n] (n a multiple of 8), s_x, and x8 = e4m3(x / s_x)
+// (bytes, same layout); fills the scale table's x entries (w_scale, s_x) and
+// scales_out[0] when given. counters[kAmaxX] must be zero on entry.
+hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_scale, void* x8,
+                          float* scales, float* scales_out, hipStream_t s);
 
 
 // GEMMs. Matrices row-major; see gemm.hip for the operand conventions.
@@ -93,13 +111,18 @@ struct GemmArgs {
   int64_t M, N, K;
   int splits;            // split-K factor (fp32 partial slabs when > 1)
   int64_t split_stride;  // elements between split slabs of C
+  const float* scale = nullptr;  // e4m3 products: device factor applied before the store
 };
 // k-splits (1 = no split) of the bf16 dW and dX products, for the tile shapes their
 // launches use; the fp32 products use gemm_f32_splits.
 int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K);
+int gemm_fp8_dw_splits(int64_t M, int64_t N, int64_t K);
+int gemm_fp8_dx_splits(int64_t M, int64_t N, int64_t K);
 int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K);
 int gemm_f32_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(Gemm kind, bool bf16, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s);
+// e4m3 operands (A, B as bytes; a.scale required), fp32 accumulation.
+hipError_t launch_gemm_fp8(Gemm kind, const GemmArgs& a, hipStream_t s);
 
 }  // namespace sce

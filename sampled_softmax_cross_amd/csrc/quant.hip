@@ -1,0 +1,104 @@
+// Per-tensor e4m3 quantisation of the activations x (bf16 [T, d]) for the fp8 step.
+//
+// The lm_head rows of "sampled_softmax.py" are an e4m3 cache and the products are
+// scaled fp8 products; x is quantised here with a power-of-two scale: s_x is the
+// smallest power of two with max|x| <= 448 s_x (448: the largest finite e4m3 value),
+// so x / s_x is exact and the conversion (round to nearest even, OCP E4M3, the
+// hardware's v_cvt_pk_fp8_f32) is the only rounding.
+//
+// Two launches: the amax of |x| over the whole tensor (atomic max of the bf16
+// magnitude bits, which order like the values), then the conversion, which derives
+// s_x from the amax in integers and writes the step's scale table.
+#include "common.h"
+#include "kernels.h"
+
+namespace sce {
+
+// Magnitude bits of the largest |x| of 8 bf16 values.
+__device__ __forceinline__ uint32_t amax8(const uint4& q) {
+  uint32_t m = 0;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, w[i] & 0x7fffu);
+    m = max(m, (w[i] >> 16) & 0x7fffu);
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(256) void k_amax_bf16(const uint4* __restrict__ x, int64_t nvec,
+                                                   int32_t* __restrict__ counters) {
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256)
+    m = max(m, amax8(x[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0 && m != 0) atomicMax(&counters[kAmaxX], (int32_t)m);
+}
+
+// s_x = 2^e from the bf16 magnitude bits of max|x|: with max|x| = f 2^E, f in [0.5, 1),
+// 448 2^e = 0.875 2^(e + 9) covers it first at e = E - 9 when f <= 0.875, else at
+// e = E - 8. f <= 0.875 is a mantissa (7 bits) of at most 0x60 (1.75 = 1 + 96/128).
+// Returns false for magnitudes outside the path's range (non-finite, or nonzero below
+// 2^-100, where 1 / s_x would leave float range).
+__device__ __forceinline__ bool x_scale_exponent(uint32_t abits, int& e) {
+  if (abits == 0) {
+    e = 0;
+    return true;
+  }
+  const int ef = (int)(abits >> 7);  // biased exponent
+  if (ef >= 255 || ef < 127 - 100) return false;
+  const int E = ef - 126;
+  e = (abits & 0x7f) <= 0x60 ? E - 9 : E - 8;
+  return true;
+}
+
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((127 + e) << 23); }
+
+__global__ __launch_bounds__(256) void k_quant_e4m3(const uint4* __restrict__ x, int64_t nvec,
+                                                    int32_t* __restrict__ counters, float w_scale,
+                                                    uint2* __restrict__ x8, float* __restrict__ scales,
+                                                    float* __restrict__ scales_out) {
+  int e = 0;
+  const bool ok = x_scale_exponent((uint32_t)counters[kAmaxX], e);
+  if (!ok) e = 0;
+  const float inv = pow2f(-e);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const float sx = pow2f(e);
+    scales[kScaleLogits] = sx * w_scale;
+    scales[kScaleX] = sx;
+    scales[kScaleW] = w_scale;
+    // s_g = 1 until the cross-entropy (which derives it from N) runs: T = 0 keeps these
+    scales[kScaleG] = 1.f;
+    scales[kScaleDx] = w_scale;
+    scales[kScaleDw] = sx;
+    if (scales_out) {
+      scales_out[0] = sx;
+      scales_out[1] = 1.f;
+    }
+    if (!ok) atomicOr(&counters[kStatus], kDevScaleRange);
+  }
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256) {
+    const uint4 q = x[i];
+    uint2 o;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(q.x) * inv, bf16_hi(q.x) * inv, 0, false);
+    o.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(q.y) * inv, bf16_hi(q.y) * inv, w, true);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(q.z) * inv, bf16_hi(q.z) * inv, 0, false);
+    o.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(q.w) * inv, bf16_hi(q.w) * inv, w, true);
+    x8[i] = o;
+  }
+}
+
+hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_scale, void* x8,
+                          float* scales, float* scales_out, hipStream_t s) {
+  const int64_t nvec = n / 8;
+  const int64_t want = (nvec + 255) / 256;
+  const int grid = (int)(want < 2048 ? (want > 0 ? want : 1) : 2048);
+  hipLaunchKernelGGL(k_amax_bf16, dim3(grid), dim3(256), 0, s, static_cast<const uint4*>(x), nvec,
+                     counters);
+  hipLaunchKernelGGL(k_quant_e4m3, dim3(grid), dim3(256), 0, s, static_cast<const uint4*>(x), nvec,
+                     counters, w_scale, static_cast<uint2*>(x8), scales, scales_out);
+  return hipGetLastError();
+}
+
+}  // namespace sce

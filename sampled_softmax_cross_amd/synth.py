@@ -114,6 +114,21 @@ def make_weights(w: Workload):
     return x, W
 
 
+def e4m3_cache(W_bits: np.ndarray):
+    """The lm_head as an e4m3 cache, as a training loop keeps one for fp8 products: one
+    float32 scale for the tensor, max|W| / 448 (the largest magnitude maps to e4m3's
+    largest finite value), and the codes of W / scale from torch's float8_e4m3fn cast
+    (round to nearest even). W_bits: bf16 bits. Returns (codes uint8 [V, d], scale)."""
+    import torch
+
+    W = bf16_bits_to_f32(W_bits)
+    scale = np.float32(np.abs(W).max() / np.float32(448.0))
+    if scale == 0:
+        scale = np.float32(1.0)
+    q = torch.from_numpy(np.ascontiguousarray(W / scale, dtype=np.float32))
+    return q.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), float(scale)
+
+
 def make_labels(w: Workload, call: int = 0):
     """(targets, prefix_targets or None) for call `call` of a workload."""
     perm = class_permutation(w.seed, w.V)

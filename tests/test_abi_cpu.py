@@ -116,3 +116,33 @@ def test_building_block_host_checks(lib):
     assert g(fake, 0, 16, fake, 4, 1, fake, 16, None, None) == 1    # empty table
     assert g(fake, 16, 16, fake, 4, 5, fake, 16, None, None) == 1   # dtype
     assert g(None, 16, 16, None, 0, 1, None, 16, None, None) == 0   # nothing to gather
+
+
+def test_fp8_host_checks(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.sce_workspace_size(16384, 768, 50304, 10240, binding.SCE_E4M3, ctypes.byref(out)) == 0
+    assert out.value >= 16384 * 10240 * 2 + 16384 * 10240          # bf16 logits + e4m3 gradient
+    assert lib.sce_workspace_size(16, 24, 100, 10, binding.SCE_E4M3, ctypes.byref(out)) == 1  # d % 16
+    f = lib.sampled_ce_forward_backward_fp8
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    args = dict(x=fake, W8=fake, ws=ctypes.c_float(0.01), y=fake, p=None, T=4, d=16, V=16, P=4,
+                stride=3, off=0, loss=fake, dX=fake, dW=fake, c=None, tp=None, pp=None, lse=None,
+                rl=None, aux=None, sc=None, wsp=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    assert call() == 2                                   # no workspace
+    assert call(ws=ctypes.c_float(0.0)) == 1             # scale must be > 0
+    assert call(ws=ctypes.c_float(float("nan"))) == 1
+    assert call(ws=ctypes.c_float(float("inf"))) == 1
+    assert call(d=8) == 1                                # d % 16 != 0
+    assert call(stride=4) == 1                           # gcd(4, 16) != 1
+    assert call(W8=None) == 1
+    assert call(x=ctypes.c_void_p((1 << 20) + 8)) == 1   # misaligned
+    assert call(wsp=fake, wsb=16) == 2                   # too small
+    g = lib.sampled_ce_forward_backward
+    assert g(fake, fake, fake, None, 4, 16, 16, 4, 3, 0, binding.SCE_E4M3, fake, fake, fake, None, None,
+             None, None, None, None, None, 0, None) == 1  # the e4m3 step has its own entry point
+

@@ -1,0 +1,129 @@
+"""The e4m3 step (sampled_ce_forward_backward_fp8) against the fp8 oracle on shapes
+that span several GEMM tiles and CE vectors with ragged tails; integers and scales
+bit for bit, floating point within bounds derived from the arithmetic (tests/fp8_tol.py),
+plus the edge cases of the scaling."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import build_candidates, fp8
+from sampled_softmax_cross_amd import binding, synth
+from tests import fp8_tol
+from tests.gpu_util import labels_dev, max_rel, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # T, d, V, P, prefix, ignore_frac, stride
+    (700, 384, 3000, 1111, True, 0.05, 7),      # d % 192 == 0: 256 x 192 dX tiles, ragged T and P
+    (300, 208, 1000, 333, True, 0.05, 7),       # d neither % 192 nor % 256: 128 x 256 dX tiles
+    (257, 144, 777, 0, True, 0.0, 1),           # full softmax, ragged V
+    (1000, 256, 3000, 1500, False, 0.0, 7),
+    (64, 768, 50304, 10240, True, 0.0, 20011),  # full vocabulary and hidden size
+    (2050, 96, 2500, 1601, False, 0.0, 3),
+    (1, 64, 100, 40, True, 0.0, 3),             # one token
+]
+
+
+def _w8(W):
+    codes, scale = synth.e4m3_cache(W)
+    return codes, scale, torch.from_numpy(codes).cuda()
+
+
+def _run(x, W8d, ws, y, p, P, stride, offset):
+    out = binding.forward_backward_fp8(to_dev(x, "bf16"), W8d, ws, labels_dev(y), labels_dev(p), P,
+                                       stride, offset, want_rows=True)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("T,d,V,P,prefix,ign,stride", CASES)
+def test_fp8_step_matches_oracle(T, d, V, P, prefix, ign, stride):
+    print(f"fp8 step T={T} d={d} V={V} P={P}", flush=True)
+    x, W, y, p = synth.small_case(T + V + P + 1, T, d, V, "bf16", prefix=prefix, ignore_frac=ign)
+    W8, ws, W8d = _w8(W)
+    offset = (T * 7) % V
+    out = _run(x, W8d, ws, y, p, P, stride, offset)
+    cand = build_candidates(V, P, stride, offset, y, p)
+    C = None if P == 0 else cand["C"]
+    ppos = cand["prefix_pos"] if p is not None else None
+    xf = synth.to_f64(x, "bf16")
+    ref = fp8.forward_backward(xf, W8, ws, C, cand["target_pos"], ppos)
+    W8C = W8 if C is None else W8[C]
+    b = fp8_tol.step_bounds(ref, ref["x8"], W8C, ws, C, cand["target_pos"], ppos)
+    # integers and scales: exact
+    if P > 0:
+        assert np.array_equal(out["C"].cpu().numpy(), cand["C"])
+    assert np.array_equal(out["target_pos"].cpu().numpy(), cand["target_pos"])
+    assert np.array_equal(out["prefix_pos"].cpu().numpy(), cand["prefix_pos"])
+    aux = out["aux"].cpu().numpy()
+    assert aux.tolist() == [cand["num_targets"], cand["N"], cand["next_offset"] if P else offset, 0]
+    sx, sg = out["scales"].cpu().numpy().astype(np.float64)
+    assert (sx, sg) == (ref["s_x"], ref["s_g"])
+    # floating point: within the derived bounds
+    got_loss = float(out["loss"].item())
+    assert abs(got_loss - ref["loss"]) <= b["loss"], (got_loss, ref["loss"], b["loss"])
+    assert (np.abs(to_f64(out["row_lse"]) - ref["L"]) <= b["row_lse"]).all()
+    assert (np.abs(to_f64(out["row_loss"]) - ref["row_loss"]) <= b["row_loss"] + 1e-6).all()
+    gX, gW = to_f64(out["dX"]), to_f64(out["dW"])
+    errX = np.abs(gX - ref["dX"])
+    rows_c = np.arange(V) if C is None else C
+    errW = np.abs(gW[rows_c] - ref["dW"][rows_c])
+    print(f"  uncertain: z {b['z_uncertain']} g8 {b['g_uncertain']} of {T * len(rows_c)}; "
+          f"max_rel dX {max_rel(gX, ref['dX']):.2e} dW {max_rel(gW, ref['dW']):.2e}; "
+          f"worst err/bound dX {np.max(errX / np.maximum(b['dX'], 1e-300)):.3f} "
+          f"dW {np.max(errW / np.maximum(b['dWC'], 1e-300)):.3f}", flush=True)
+    assert (errX <= b["dX"]).all()
+    assert (errW <= b["dWC"]).all()
+    if P > 0:
+        outside = np.setdiff1d(np.arange(V), cand["C"])
+        raw = out["dW"].cpu().view(torch.int16).numpy()
+        assert (raw[outside] == 0).all()
+
+
+def test_fp8_p0_equals_pv_bitwise():
+    T, d, V = 300, 64, 1000
+    x, W, y, p = synth.small_case(31, T, d, V, "bf16", prefix=True, ignore_frac=0.1)
+    _, ws, W8d = _w8(W)
+    a = _run(x, W8d, ws, y, p, 0, 7, 0)
+    c = _run(x, W8d, ws, y, p, V, 7, 0)
+    for k in ("loss", "dX", "dW", "row_lse", "row_loss", "target_pos", "prefix_pos", "scales"):
+        assert torch.equal(a[k], c[k]), k
+
+
+def test_fp8_no_labels_and_empty():
+    T, d, V, P = 200, 64, 500, 100
+    x, W, y, p = synth.small_case(32, T, d, V, "bf16", prefix=True)
+    _, ws, W8d = _w8(W)
+    y[:] = -1
+    p[:] = -1
+    out = _run(x, W8d, ws, y, p, P, 7, 3)
+    assert float(out["loss"].item()) == 0.0
+    assert not out["dX"].any() and not out["dW"].any()
+    assert out["aux"][1].item() == 0
+    assert out["scales"][1].item() == 1.0                     # s_g = 1 when N = 0
+    # T = 0: nothing to quantise; dW cleared, s_x = s_g = 1
+    x0 = torch.empty(0, d, dtype=torch.bfloat16, device="cuda")
+    y0 = torch.empty(0, dtype=torch.int64, device="cuda")
+    o0 = binding.forward_backward_fp8(x0, W8d, ws, y0, None, P, 7, 3)
+    torch.cuda.synchronize()
+    assert float(o0["loss"].item()) == 0.0 and not o0["dW"].any()
+    assert o0["scales"].tolist() == [1.0, 1.0]
+
+
+def test_fp8_scale_range_flag():
+    T, d, V, P = 64, 64, 300, 64
+    x, W, y, p = synth.small_case(33, T, d, V, "bf16", prefix=False)
+    _, ws, W8d = _w8(W)
+    xd = to_dev(x, "bf16")
+    xd[3, 5] = float("nan")
+    out = binding.forward_backward_fp8(xd, W8d, ws, labels_dev(y), None, P, 7, 0)
+    torch.cuda.synchronize()
+    assert int(out["aux"][3].item()) & binding.DEV_SCALE_RANGE
+    xt = torch.full((T, d), 2.0 ** -110, dtype=torch.bfloat16, device="cuda")  # below 2^-100
+    out = binding.forward_backward_fp8(xt, W8d, ws, labels_dev(y), None, P, 7, 0)
+    torch.cuda.synchronize()
+    assert int(out["aux"][3].item()) & binding.DEV_SCALE_RANGE
+    out = binding.forward_backward_fp8(to_dev(x, "bf16"), W8d, ws, labels_dev(y), None, P, 7, 0)
+    torch.cuda.synchronize()
+    assert int(out["aux"][3].item()) == 0
