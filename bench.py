@@ -1,10 +1,12 @@
 """Benchmark of the sampled-softmax cross-entropy step on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage01]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage01] [--dtype e4m3]
 
 A step is one call of sampled_ce_forward_backward: candidate build, row gather,
 logits GEMM, fused CE forward/backward, dX and dW GEMMs, dense scatter, over one
-microbatch of synthetic inputs already resident in HBM. Prints ONE JSON line:
+microbatch of synthetic inputs already resident in HBM. --dtype e4m3 times
+sampled_ce_forward_backward_fp8 on the same microbatch instead (the lm_head as an
+e4m3 cache with one scale, x quantised per call, e4m3 products). Prints ONE JSON line:
 tokens/s of the whole step, the roofline fraction of its dominant kernel (timed
 live with HIP events the library records on the call's stream), the same library
 at P = V for the speedup of the sampled path, and the CPU oracle on a bounded
@@ -22,24 +24,26 @@ if ROOT not in sys.path:
 
 METRIC = "tokens/s sampled-CE fwd+bwd (V=50304,d=768,P=10240/14336/24576); % roofline"
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "e4m3": 5000.0}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_work(w, P_eff):
+def stage_work(w, P_eff, e4m3=False):
     """Algorithmic work of one launch of each stage: (kind, amount)."""
     es = 2 if w.dtype == "bf16" else 4
     ldz = (P_eff + 7) // 8 * 8
     flops = 2.0 * w.T * P_eff * w.d
+    # read Z once, write dZ once (e4m3 step: read bf16 Z, write the e4m3 gradient), plus
+    # labels and the row loss
+    ce_bytes = (w.T * ldz * 3.0 if e4m3 else 2.0 * w.T * ldz * es) + w.T * 12
     return {
         "logits": ("mfma", flops),
         "dx": ("mfma", flops),
         "dw": ("mfma", flops),
-        # read Z once, write dZ once, plus labels and the row loss
-        "ce": ("hbm", 2.0 * w.T * ldz * es + w.T * 12),
+        "ce": ("hbm", ce_bytes),
 
         # read the fp32 candidate-row gradient once, write the dense dW, read vocab_pos
         "scatter": ("hbm", P_eff * w.d * 4.0 + w.V * w.d * es + 4 * w.V),
@@ -83,6 +87,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="stage01")
+    ap.add_argument("--dtype", choices=["auto", "e4m3"], default="auto",
+                    help="auto: the workload's own precision (bf16 or f32); e4m3: the e4m3 "
+                         "operand step on the same bf16 microbatch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
@@ -119,13 +126,23 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
+    e4m3 = args.dtype == "e4m3"
+    if e4m3 and w.dtype != "bf16":
+        raise SystemExit("--dtype e4m3 needs a bf16 workload")
     xd, Wd = to_dev(x), to_dev(W)
     yd = torch.from_numpy(y).to(dev)
     pd = torch.from_numpy(p).to(dev) if p is not None else None
     off = w.offset
     outs = {}
+    if e4m3:
+        W8, w_scale = synth.e4m3_cache(W)
+        W8d = torch.from_numpy(W8).to(dev)
+        log(f"[bench] e4m3 products: lm_head cache scale {w_scale:.4g}")
 
     def step(P):
+        if e4m3:
+            return binding.forward_backward_fp8(xd, W8d, w_scale, yd, pd, P, w.stride, off,
+                                                outputs=outs.get(P))
         return binding.forward_backward(xd, Wd, yd, pd, P, w.stride, off, outputs=outs.get(P))
 
     def timed(P, steps, warmup):
@@ -159,7 +176,8 @@ def main():
     stage_ms, ncalls = binding.profile_collect()
     stage_ms = {k: v / ncalls for k, v in stage_ms.items()}
     P_eff = w.P if w.P else w.V
-    work = stage_work(w, P_eff)
+    work = stage_work(w, P_eff, e4m3)
+    ptype = "e4m3" if e4m3 else w.dtype
     stages = {}
     for k, t in stage_ms.items():
         entry = {"ms": round(t, 5)}
@@ -167,7 +185,7 @@ def main():
             kind, amount = work[k]
             if kind == "mfma":
                 ach = amount / (t * 1e-3) / 1e12
-                entry.update(tflops=round(ach, 2), frac=round(ach / PEAK_TFLOPS[w.dtype], 4))
+                entry.update(tflops=round(ach, 2), frac=round(ach / PEAK_TFLOPS[ptype], 4))
             else:
                 ach = amount / (t * 1e-3) / 1e9
                 entry.update(gbs=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 4))
@@ -178,8 +196,8 @@ def main():
     if kind == "mfma":
         achieved = amount / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4),
+                "peak": PEAK_TFLOPS[ptype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[ptype], 4),
                 "traffic": recorded_traffic(w.name, dom)}
     else:
         achieved = amount / (stage_ms[dom] * 1e-3) / 1e9
@@ -206,7 +224,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, x, W, y, p, args.cpu_sample_tokens)
+        cpu = cpu_baseline(w, x, W, y, p, args.cpu_sample_tokens, e4m3)
         log(f"[bench] cpu oracle: {cpu}")
 
     line = {
@@ -220,11 +238,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": ptype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "V": w.V, "P": w.P,
                    "stride": w.stride, "offset": off, "targets": f"zipf({w.zipf_s})",
-                   "prefix_targets": w.prefix},
+                   "prefix_targets": w.prefix,
+                   **({"operands": "e4m3 x and lm_head, bf16 logits"} if e4m3 else {})},
         "roofline": roof,
         "stages": stages,
         "full_softmax_same_library": full_cmp,
@@ -310,12 +329,13 @@ def micro(kind):
                               "torch_index_select_us": round(ms_t * 1e3, 2)}), flush=True)
 
 
-def cpu_baseline(w, x, W, y, p, sample_tokens):
+def cpu_baseline(w, x, W, y, p, sample_tokens, e4m3=False):
     """The float64 CPU oracle, as it stands, on the first `sample_tokens` tokens of the
-    same microbatch: candidate build + dense loss and gradients."""
+    same microbatch: candidate build + dense loss and gradients (the e4m3 oracle for the
+    e4m3 step)."""
     from threadpoolctl import threadpool_info
 
-    from oracle import build_candidates, ce
+    from oracle import build_candidates, ce, fp8
     from sampled_softmax_cross_amd import synth
 
     Ts = min(sample_tokens, w.T)
@@ -323,16 +343,23 @@ def cpu_baseline(w, x, W, y, p, sample_tokens):
     Wf = synth.to_f64(W, w.dtype)
     ys = y[:Ts]
     ps = None if p is None else p[:Ts]
+    if e4m3:
+        W8, w_scale = synth.e4m3_cache(W)
     t0 = time.perf_counter()
     cand = build_candidates(w.V, w.P, w.stride, w.offset, ys, ps)
-    ce.forward_backward(xs, Wf, None if w.P == 0 else cand["C"], cand["target_pos"],
-                        cand["prefix_pos"] if ps is not None else None)
+    C = None if w.P == 0 else cand["C"]
+    ppos = cand["prefix_pos"] if ps is not None else None
+    if e4m3:
+        fp8.forward_backward(xs, W8, w_scale, C, cand["target_pos"], ppos)
+    else:
+        ce.forward_backward(xs, Wf, C, cand["target_pos"], ppos)
     dt = time.perf_counter() - t0
     threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     return {"value": round(Ts / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"first {Ts} of {w.T} tokens of the {w.name} microbatch (same P, V, d, "
-                      f"stride, offset): candidate build + float64 loss, dX, dW"}
+                      f"stride, offset): candidate build + float64 loss, dX, dW"
+                      + (" of the e4m3 step" if e4m3 else "")}
 
 
 if __name__ == "__main__":

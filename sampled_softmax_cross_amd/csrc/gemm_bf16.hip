@@ -94,8 +94,11 @@ __device__ __forceinline__ int km_index(int k, int ch) {
 }
 
 // One operand tile of R rows (r-major) or R columns (k-major) by SK k per stage of
-// EB-byte elements, filled by NW waves (64 chunks of 16 B per instruction).
-template <int R, bool KMAJ, int NW, int SK, int EB>
+// EB-byte elements, filled by NW waves (64 chunks of 16 B per instruction). With KEEP
+// the lanes' chunk offsets are computed once and held in registers; otherwise they
+// are recomputed at every issue from an opaque lane id (a few integer operations per
+// instruction), which frees 2 * kN registers for tiles that would otherwise spill.
+template <int R, bool KMAJ, int NW, int SK, int EB, bool KEEP = true>
 struct DmaTile {
   static constexpr int CPR = SK * EB / 16;  // chunks per r-major row
   static constexpr int RB = R * EB;         // bytes per k-major row
@@ -104,26 +107,34 @@ struct DmaTile {
                     (!KMAJ || RB % 256 == 0 || RB == 384 || (EB == 1 && (RB % 128 == 0 || RB == 192))),
                 "tile shape");
   static constexpr int kN = R * SK * EB / (1024 * NW);  // DMA instructions per wave per stage
-  int off[kN];  // byte offset of the lane's chunk from the tile origin
-  int kr[kN];   // (k << 16) | row of the lane's chunk, for the clip: k of the chunk
-                // (r-major) or its row (k-major), and its row (r-major) or first column
-  int w;        // index of this wave among the NW that fill the tile
-  __device__ __forceinline__ void init(int64_t ld, int wave) {
-    const int lane = threadIdx.x & 63;
+  int off[KEEP ? kN : 1];  // byte offset of the lane's chunk from the tile origin
+  int kr[KEEP ? kN : 1];   // (k << 16) | row of the lane's chunk, for the clip: k of the chunk
+                           // (r-major) or its row (k-major), and its row (r-major) or first column
+  int w;                   // index of this wave among the NW that fill the tile
+  int64_t ld;
+  // (k, r) of chunk i of this wave for lane `lane`
+  __device__ __forceinline__ static void chunk(int wv, int i, int lane, int& k, int& r) {
+    const int q = 64 * (wv * kN + i) + lane;  // linear LDS chunk this lane fills
+    if constexpr (!KMAJ) {
+      r = q / CPR;
+      k = ((q % CPR) ^ rm_swizzle<CPR>(r)) * EPC;
+    } else {
+      k = q / (RB / 16);
+      r = ((q % (RB / 16)) ^ km_swizzle<RB, EB>(k)) * EPC;
+    }
+  }
+  __device__ __forceinline__ void init(int64_t ld_, int wave) {
     w = wave;
+    ld = ld_;
+    if constexpr (KEEP) {
+      const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int q = 64 * (w * kN + i) + lane;  // linear LDS chunk this lane fills
-      int r, k;
-      if constexpr (!KMAJ) {
-        r = q / CPR;
-        k = ((q % CPR) ^ rm_swizzle<CPR>(r)) * EPC;
-      } else {
-        k = q / (RB / 16);
-        r = ((q % (RB / 16)) ^ km_swizzle<RB, EB>(k)) * EPC;
+      for (int i = 0; i < kN; ++i) {
+        int k, r;
+        chunk(w, i, lane, k, r);
+        kr[i] = (k << 16) | r;
+        off[i] = (int)((KMAJ ? (int64_t)k * ld + r : (int64_t)r * ld + k) * EB);
       }
-      kr[i] = (k << 16) | r;
-      off[i] = (int)((KMAJ ? (int64_t)k * ld + r : (int64_t)r * ld + k) * EB);
     }
   }
   // base: address of tile element (0, 0) of this stage; rows_valid / k_valid clip the
@@ -131,11 +142,26 @@ struct DmaTile {
   __device__ __forceinline__ void issue(const void* base, int64_t rows_valid, int64_t k_valid,
                                         uint4* tile) const {
     const rsrc_t rs = make_rsrc(base);
+    int lane = 0;
+    if constexpr (!KEEP) {
+      lane = threadIdx.x & 63;
+      asm volatile("" : "+v"(lane));  // keep the recomputation here, not hoisted into registers
+    }
 #pragma unroll
-    for (int i = 0; i < kN; ++i)
+    for (int i = 0; i < kN; ++i) {
+      int o, kk, rr;
+      if constexpr (KEEP) {
+        o = off[i];
+        kk = kr[i] >> 16;
+        rr = kr[i] & 0xffff;
+      } else {
+        chunk(w, i, lane, kk, rr);
+        o = (int)(KMAJ ? kk * (int)ld + rr : rr * (int)ld + kk) * EB;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(tile + (w * kN + i) * 64), 16,
-          ((kr[i] >> 16) < k_valid && (kr[i] & 0xffff) < rows_valid) ? off[i] : kOOB, 0, 0, 0);
+          (kk < k_valid && rr < rows_valid) ? o : kOOB, 0, 0, 0);
+    }
   }
 };
 
@@ -264,8 +290,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
     return c;
   };
 
-  DmaTile<BM, A_KM, NW, SK, EB> ta;
-  DmaTile<BN, B_KM, NW, SK, EB> tb;
+  // e4m3 waves with 8 accumulator blocks recompute their DMA offsets: their fragments
+  // are twice bf16's, and spilled registers would be reloaded with vector loads that
+  // wait on the DMA queue (measured 1.3x slower dW at S2-late shapes)
+  constexpr bool kKeepOffsets = EB == 2 || TM * TN < 8;
+  DmaTile<BM, A_KM, NW, SK, EB, kKeepOffsets> ta;
+  DmaTile<BN, B_KM, NW, SK, EB, kKeepOffsets> tb;
   const char* const Ab = static_cast<const char*>(A);
   const char* const Bb = static_cast<const char*>(B);
   ta.init(lda, wid);

@@ -26,14 +26,27 @@ __device__ __forceinline__ uint32_t amax8(const uint4& q) {
   return m;
 }
 
+// One atomic per workgroup (atomics on one address serialise: one per wave over a
+// 25 MB tensor measured 98 us), four loads in flight per lane.
 __global__ __launch_bounds__(256) void k_amax_bf16(const uint4* __restrict__ x, int64_t nvec,
                                                    int32_t* __restrict__ counters) {
+  __shared__ uint32_t wmax[256 / kWave];
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += (int64_t)gridDim.x * 256)
-    m = max(m, amax8(x[i]));
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    const uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+    m = max(m, max(max(amax8(a), amax8(b)), max(amax8(c), amax8(d))));
+  }
+  for (; i < nvec; i += stride) m = max(m, amax8(x[i]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
-  if ((threadIdx.x & (kWave - 1)) == 0 && m != 0) atomicMax(&counters[kAmaxX], (int32_t)m);
+  if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (m != 0) atomicMax(&counters[kAmaxX], (int32_t)m);
+  }
 }
 
 // s_x = 2^e from the bf16 magnitude bits of max|x|: with max|x| = f 2^E, f in [0.5, 1),
@@ -94,7 +107,8 @@ hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_s
   const int64_t nvec = n / 8;
   const int64_t want = (nvec + 255) / 256;
   const int grid = (int)(want < 2048 ? (want > 0 ? want : 1) : 2048);
-  hipLaunchKernelGGL(k_amax_bf16, dim3(grid), dim3(256), 0, s, static_cast<const uint4*>(x), nvec,
+  const int agrid = grid < 512 ? grid : 512;
+  hipLaunchKernelGGL(k_amax_bf16, dim3(agrid), dim3(256), 0, s, static_cast<const uint4*>(x), nvec,
                      counters);
   hipLaunchKernelGGL(k_quant_e4m3, dim3(grid), dim3(256), 0, s, static_cast<const uint4*>(x), nvec,
                      counters, w_scale, static_cast<uint2*>(x8), scales, scales_out);
