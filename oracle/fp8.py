@@ -177,6 +177,27 @@ def lse_rows(xv, WCv, s_xw, block=2048):
     return out
 
 
+def label_logits(xv, WCv, s_xw, pos):
+    """bf16 logit z[t, pos[t]] for every t with pos[t] >= 0 (0 elsewhere)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    out = np.zeros(pos.shape[0])
+    ok = pos >= 0
+    out[ok] = bf16_round(s_xw * np.einsum("td,td->t", xv[ok], WCv[pos[ok]]))
+    return out
+
+
+def loss_from_lse(xv, WCv, s_xw, L, target_pos, prefix_pos=None):
+    """(loss, row_loss, N) given every row's L: the label terms L - z over the bf16 logits."""
+    tpos = np.asarray(target_pos, dtype=np.int64)
+    row_loss = np.where(tpos >= 0, L - label_logits(xv, WCv, s_xw, tpos), 0.0)
+    N = int((tpos >= 0).sum())
+    if prefix_pos is not None:
+        ppos = np.asarray(prefix_pos, dtype=np.int64)
+        row_loss = row_loss + np.where(ppos >= 0, L - label_logits(xv, WCv, s_xw, ppos), 0.0)
+        N += int((ppos >= 0).sum())
+    return (float(row_loss.sum() / N) if N else 0.0), row_loss, N
+
+
 def g8_rows(z, L, tpos, ppos, N, s_g):
     """e4m3 codes of g / s_g for rows whose bf16 logits z and row log-sum-exp L are given."""
     tpos = np.asarray(tpos, dtype=np.int64)

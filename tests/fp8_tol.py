@@ -81,66 +81,126 @@ def mfma_e4m3_error(a, b):
     return cut + adds
 
 
-def step_bounds(ref, x8, W8C, w_scale, C, target_pos, prefix_pos):
-    """Per-element bounds on |kernel - oracle| for one e4m3 step computed densely by
-    oracle.fp8.forward_backward (`ref`; C the candidate classes or None): returns a dict
-    with dX [T,d], dWC [P,d] (the rows of C in dW), row_lse [T], loss, and the counts
-    of values that may round either way."""
-    xv = fp8.e4m3_decode(x8)
-    Wv = fp8.e4m3_decode(W8C)
-    T, d = xv.shape
-    P = Wv.shape[0]
-    s_x, s_g, N = ref["s_x"], ref["s_g"], ref["N"]
-    s_xw = s_x * float(np.float32(w_scale))
-    z_exact, z, L = ref["z_exact"], ref["z"], ref["L"]
+def _rows_block(xb, Wv, s_xw, s_g, N, tp, pp, L):
+    """The per-row part of the bounds for a block of rows (decoded x8 rows xb, their label
+    positions tp / pp or None, and the oracle's L for them)."""
+    T, d = xb.shape
+    z_exact = s_xw * (xb @ Wv.T)
     # logits: the product's sum, then the scale product
-    eps_z = s_xw * mfma_e4m3_error(xv, Wv.T) + U * np.abs(z_exact)
+    eps_z = s_xw * mfma_e4m3_error(xb, Wv.T) + U * np.abs(z_exact)
+    z = fp8.bf16_round(z_exact)
     zdist, zstep = bf16_midpoint_distance(z_exact)
-    z_unc = zdist <= eps_z
-    z_dev = z_unc * (eps_z + zstep)           # how far an uncertain logit may land
+    z_dev = (zdist <= eps_z) * (eps_z + zstep)   # how far an uncertain logit may land
+    P = Wv.shape[0]
     # row log-sum-exp: exp2 arguments, exp2, a P-term sum, the lane merges, log2
     p = np.exp(z - L[:, None])
-    flip_L = (p * np.expm1(z_dev)).sum(axis=1)
     eps_L = (2 * P * U + 64 * U + 2 * U * np.abs(z).max(axis=1) + 4 * U * np.abs(L - z.max(axis=1))
-             + U * np.abs(L) + flip_L)
+             + U * np.abs(L) + (p * np.expm1(z_dev)).sum(axis=1))
     # gradient in units of s_g: softmax part and one-hot part
-    tp = np.asarray(target_pos, dtype=np.int64)
+    rows = np.arange(T)
     n = (tp >= 0).astype(np.float64)
     onehot = np.zeros_like(z)
-    rows = np.arange(T)
     onehot[rows[tp >= 0], tp[tp >= 0]] += 1
-    if prefix_pos is not None:
-        pp = np.asarray(prefix_pos, dtype=np.int64)
+    zlab = np.zeros(T)
+    zlab[tp >= 0] += z_dev[rows[tp >= 0], tp[tp >= 0]]
+    if pp is not None:
         n = n + (pp >= 0)
         np.add.at(onehot, (rows[pp >= 0], pp[pp >= 0]), 1)
+        zlab[pp >= 0] += z_dev[rows[pp >= 0], pp[pp >= 0]]
     if N:
         v_soft = n[:, None] * p / (N * s_g)
+        v = (n[:, None] * p - onehot) / N / s_g
         v_oh = onehot / (N * s_g)
     else:
-        v_soft = v_oh = np.zeros_like(z)
-    v = ref["g_scaled"]
+        v_soft = v_oh = v = np.zeros_like(z)
     eps_v = (v_soft * (eps_L[:, None] + 6 * U + 2 * U * np.abs(z) + np.expm1(z_dev))
              + 2 * U * v_oh + U * np.abs(v))
     gdist, gstep = e4m3_midpoint_distance(v)
     g_unc = gdist <= eps_v
-    g_dev = g_unc * (eps_v + gstep)           # how far an uncertain code's value may land
-    g8v = fp8.e4m3_decode(ref["g8"])
-    # products: moved codes, the product's sum, then the output rounding
-    cdx = s_g * float(np.float32(w_scale))
-    dx_dev = cdx * (g_dev @ np.abs(Wv) + mfma_e4m3_error(g8v, Wv))
-    bdx = 2.0 ** -8 * np.abs(ref["dX"]) + (1 + 2.0 ** -8) * dx_dev + 2 * U * np.abs(ref["dX"])
-    cdw = s_g * s_x
+    g_dev = g_unc * (eps_v + gstep)              # how far an uncertain code's value may land
+    g8v = fp8.e4m3_decode(fp8.e4m3_encode(v))
+    return dict(eps_L=eps_L, n=n, zlab=zlab, g_dev=g_dev, g8v=g8v,
+                z_uncertain=int((z_dev > 0).sum()), g_uncertain=int(g_unc.sum()))
+
+
+def _dx_bound(dx_ref, g_dev, g8v, Wv, cdx):
+    dev = cdx * (g_dev @ np.abs(Wv) + mfma_e4m3_error(g8v, Wv))
+    return 2.0 ** -8 * np.abs(dx_ref) + (1 + 2.0 ** -8) * dev + 2 * U * np.abs(dx_ref)
+
+
+def _dw_bound(dw_ref, dev):
+    return 2.0 ** -8 * np.abs(dw_ref) + (1 + 2.0 ** -8) * dev + 2 * U * np.abs(dw_ref)
+
+
+def _loss_bound(n, eps_L, zlab, row_loss, loss, N, T):
+    if not N:
+        return 0.0
+    return ((n * eps_L + zlab).sum() + 2 * T * U * np.abs(row_loss).sum()) / N + U * abs(loss)
+
+
+def step_bounds(ref, x8, W8C, w_scale, C, target_pos, prefix_pos):
+    """Per-element bounds on |kernel - oracle| for one e4m3 step computed densely by
+    oracle.fp8.forward_backward (`ref`; C the candidate classes or None): returns a dict
+    with dX [T,d], dWC [P,d] (the rows of C in dW), row_lse [T], row_loss [T], loss, and
+    the counts of values that may round either way."""
+    xv = fp8.e4m3_decode(x8)
+    Wv = fp8.e4m3_decode(W8C)
+    T = xv.shape[0]
+    s_x, s_g, N = ref["s_x"], ref["s_g"], ref["N"]
+    w = float(np.float32(w_scale))
+    tp = np.asarray(target_pos, dtype=np.int64)
+    pp = None if prefix_pos is None else np.asarray(prefix_pos, dtype=np.int64)
+    b = _rows_block(xv, Wv, s_x * w, s_g, N, tp, pp, ref["L"])
+    bdx = _dx_bound(ref["dX"], b["g_dev"], b["g8v"], Wv, s_g * w)
     # dW: k-split partials (at most 8) add in float32 in the reduction as well
-    dw_dev = cdw * (g_dev.T @ np.abs(xv) + mfma_e4m3_error(g8v.T, xv)
-                    + 16 * U * (np.abs(g8v).T @ np.abs(xv)))
-    # loss: per-row L errors, uncertain label logits, the fp32 sum of T terms
-    zlab = np.zeros(T)
-    zlab[tp >= 0] += z_dev[rows[tp >= 0], tp[tp >= 0]]
-    if prefix_pos is not None:
-        zlab[pp >= 0] += z_dev[rows[pp >= 0], pp[pp >= 0]]
-    row_err = n * eps_L + zlab
-    bloss = ((row_err.sum() + 2 * T * U * np.abs(ref["row_loss"]).sum()) / N + U * abs(ref["loss"])) if N else 0.0
+    cdw = s_g * s_x
+    dev = cdw * (b["g_dev"].T @ np.abs(xv) + mfma_e4m3_error(b["g8v"].T, xv)
+                 + 16 * U * (np.abs(b["g8v"]).T @ np.abs(xv)))
     ref_dwc = ref["dW"] if C is None else ref["dW"][np.asarray(C, dtype=np.int64)]
-    bdw = 2.0 ** -8 * np.abs(ref_dwc) + (1 + 2.0 ** -8) * dw_dev + 2 * U * np.abs(ref_dwc)
-    return dict(dX=bdx, dWC=bdw, row_lse=eps_L, row_loss=row_err, loss=bloss,
-                z_uncertain=int(z_unc.sum()), g_uncertain=int(g_unc.sum()))
+    return dict(dX=bdx, dWC=_dw_bound(ref_dwc, dev), row_lse=b["eps_L"],
+                row_loss=b["n"] * b["eps_L"] + b["zlab"],
+                loss=_loss_bound(b["n"], b["eps_L"], b["zlab"], ref["row_loss"], ref["loss"], N, T),
+                z_uncertain=b["z_uncertain"], g_uncertain=b["g_uncertain"])
+
+
+def sampled_bounds(x8, W8C, w_scale, s_x, s_g, N, target_pos, prefix_pos, L, rows, cols,
+                   dx_ref, dwc_ref, row_loss, loss, block=2048):
+    """The same bounds at full size, block by block over the rows: dX on `rows` (dx_ref:
+    the oracle's values there), dW_C on candidate positions `cols` (dwc_ref), the loss and
+    every row's L (L: the oracle's values)."""
+    xv = fp8.e4m3_decode(x8)
+    Wv = fp8.e4m3_decode(W8C)
+    T, d = xv.shape
+    w = float(np.float32(w_scale))
+    tp_all = np.asarray(target_pos, dtype=np.int64)
+    pp_all = None if prefix_pos is None else np.asarray(prefix_pos, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    eps_L = np.zeros(T)
+    lb = 0.0
+    dx_b = np.zeros((rows.shape[0], d))
+    dw_flip = np.zeros((cols.shape[0], d))
+    gmax_g = []
+    gmax_x = []
+    dw_abs = np.zeros((cols.shape[0], d))
+    for r0 in range(0, T, block):
+        r1 = min(T, r0 + block)
+        b = _rows_block(xv[r0:r1], Wv, s_x * w, s_g, N, tp_all[r0:r1],
+                        None if pp_all is None else pp_all[r0:r1], L[r0:r1])
+        eps_L[r0:r1] = b["eps_L"]
+        lb += (b["n"] * b["eps_L"] + b["zlab"]).sum()
+        sel = (rows >= r0) & (rows < r1)
+        if sel.any():
+            rr = rows[sel] - r0
+            dx_b[sel] = _dx_bound(dx_ref[sel], b["g_dev"][rr], b["g8v"][rr], Wv, s_g * w)
+        gc = b["g8v"][:, cols]
+        xb = xv[r0:r1]
+        dw_flip += b["g_dev"][:, cols].T @ np.abs(xb)
+        dw_abs += np.abs(gc).T @ np.abs(xb)
+        gmax_g.append(_group_max(gc, 0))
+        gmax_x.append(_group_max(xb, 0))
+    cut = 7 * 2.0 ** -13 * (np.concatenate(gmax_g).T @ np.concatenate(gmax_x))
+    cdw = s_g * s_x
+    dev = cdw * (dw_flip + cut + (2 * ((T + 7) // 8 + 8) + 16) * U * dw_abs)
+    loss_b = ((lb + 2 * T * U * np.abs(row_loss).sum()) / N + U * abs(loss)) if N else 0.0
+    return dict(dX=dx_b, dWC=_dw_bound(dwc_ref, dev), row_lse=eps_L, loss=loss_b)

@@ -127,3 +127,58 @@ def test_fp8_scale_range_flag():
     out = binding.forward_backward_fp8(to_dev(x, "bf16"), W8d, ws, labels_dev(y), None, P, 7, 0)
     torch.cuda.synchronize()
     assert int(out["aux"][3].item()) == 0
+
+
+def test_fp8_stage01_full_size():
+    """The stage-0/1 workload (T=16384, d=768, V=50304, P=10240) in the launch
+    configuration the benchmark times: integers and scales exactly; every row's L, the
+    loss, sampled dX rows and sampled dW rows of C within the derived bounds; every row
+    of dW outside C exactly zero."""
+    w = synth.workload("stage01")
+    x, W = synth.make_weights(w)
+    y, p = synth.make_labels(w, 0)
+    W8, ws, W8d = _w8(W)
+    off = w.offset
+    out = binding.forward_backward_fp8(to_dev(x, "bf16"), W8d, ws, labels_dev(y), labels_dev(p), w.P,
+                                       w.stride, off, want_rows=True)
+    torch.cuda.synchronize()
+    cand = build_candidates(w.V, w.P, w.stride, off, y, p)
+    C, tp = cand["C"], cand["target_pos"]
+    pp = cand["prefix_pos"] if p is not None else None
+    assert np.array_equal(out["C"].cpu().numpy(), C)
+    assert np.array_equal(out["target_pos"].cpu().numpy(), tp)
+    aux = out["aux"].cpu().numpy().tolist()
+    assert aux == [cand["num_targets"], cand["N"], cand["next_offset"], 0]
+    xf = synth.to_f64(x, "bf16")
+    x8, s_x = fp8.quantize_x(xf)
+    N = cand["N"]
+    s_g = fp8.grad_scale(N, 2 if p is not None else 1)
+    assert out["scales"].cpu().numpy().astype(np.float64).tolist() == [s_x, s_g]
+    xv = fp8.e4m3_decode(x8)
+    Wv = fp8.e4m3_decode(W8[C])
+    s_xw = s_x * float(np.float32(ws))
+    L = fp8.lse_rows(xv, Wv, s_xw)
+    loss, row_loss, N2 = fp8.loss_from_lse(xv, Wv, s_xw, L, tp, pp)
+    assert N2 == N
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, w.T - 1], rng.integers(0, w.T, 29)]))
+    top = np.bincount(tp[tp >= 0], minlength=w.P).argsort()[-8:]
+    cols = np.unique(np.concatenate([[0, w.P - 1], rng.integers(0, w.P, 22), top]))
+    dx_ref = fp8.dx_rows(xv, Wv, s_xw, L, tp, pp, N, s_g, ws, rows)
+    dwc_ref = fp8.dwc_rows(xv, Wv, s_xw, L, tp, pp, N, s_g, s_x, cols)
+    b = fp8_tol.sampled_bounds(x8, W8[C], ws, s_x, s_g, N, tp, pp, L, rows, cols, dx_ref, dwc_ref,
+                               row_loss, loss)
+    got = float(out["loss"].item())
+    print(f"  loss {got:.7f} oracle {loss:.7f} bound {b['loss']:.2e}", flush=True)
+    assert abs(got - loss) <= b["loss"]
+    assert (np.abs(to_f64(out["row_lse"]) - L) <= b["row_lse"]).all()
+    gX = to_f64(out["dX"][torch.from_numpy(rows).cuda()])
+    gW = to_f64(out["dW"][torch.from_numpy(C[cols]).cuda()])
+    ex, ew = np.abs(gX - dx_ref), np.abs(gW - dwc_ref)
+    print(f"  dX rows max_rel {max_rel(gX, dx_ref):.2e} worst err/bound {np.max(ex / b['dX']):.3f}; "
+          f"dW rows max_rel {max_rel(gW, dwc_ref):.2e} worst err/bound {np.max(ew / b['dWC']):.3f}",
+          flush=True)
+    assert (ex <= b["dX"]).all()
+    assert (ew <= b["dWC"]).all()
+    outside = np.setdiff1d(np.arange(w.V), C)
+    assert (out["dW"].view(torch.int16).cpu().numpy()[outside] == 0).all()
