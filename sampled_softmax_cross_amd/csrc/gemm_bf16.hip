@@ -279,9 +279,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
   struct Unit {
     int64_t m0, n0, kb, ke;
   };
+  const int gm = group_rows(nbx, (int64_t)BM * BN * (OUT == kOutBF16 ? 2 : 4));
   auto unit = [&](int i) {
     int tm, tn, sp;
-    unit_of((int)blockIdx.x + i * G, nby, nbx, splits, tm, tn, sp);
+    unit_of((int)blockIdx.x + i * G, nby, nbx, splits, gm, tm, tn, sp);
     Unit c;
     c.m0 = (int64_t)tm * BM;
     c.n0 = (int64_t)tn * BN;

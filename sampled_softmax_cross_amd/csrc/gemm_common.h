@@ -56,13 +56,27 @@ __device__ __forceinline__ void tile_of(int bid, int nby, int nbx, int& tm, int&
   tn = in / gsize;
 }
 
+// Rows per group of the tile order for outputs of many column tiles. Within a group the
+// order walks all nbx column tiles for `g` rows, so a B (column) tile is reused after the
+// XCD has written g * nbx output tiles; chip-wide that is g * nbx * tile_bytes * 8 bytes of
+// output streaming through the 256 MB MALL. The largest g in {8, 4, 2} that keeps this
+// under the MALL's size lets the reused B tiles still hit there; when none does, 8 (the
+// best L2 reuse of the A rows). Measured on the logits products: 5-18% faster than a
+// fixed 8 at P = 14336 and 24576 (T = 49152), equal elsewhere.
+__device__ __forceinline__ int group_rows(int nbx, int64_t tile_bytes) {
+  constexpr int64_t kMall = 256ll << 20;
+  for (int g = 8; g >= 2; g >>= 1)
+    if ((int64_t)g * nbx * tile_bytes * kNumXcd <= kMall) return g;
+  return 8;
+}
+
 // Tile and k-range of unit u among nby x nbx tiles x `splits` k-ranges. Units are
 // renumbered XCD-contiguously (workgroup ids are dealt round-robin over the XCDs) with the
 // k-range outermost, so each XCD works on one k-range. Within a k-range, tiles go
 // row-major when there are at most 4 column tiles (every column tile of a row shares the
-// row's A block, and they land on the same XCD), otherwise in groups of kGroupM rows.
-__device__ __forceinline__ void unit_of(int u, int nby, int nbx, int splits, int& tm, int& tn,
-                                        int& split) {
+// row's A block, and they land on the same XCD), otherwise in groups of `gm` rows.
+__device__ __forceinline__ void unit_of(int u, int nby, int nbx, int splits, int gm, int& tm,
+                                        int& tn, int& split) {
   const int ntiles = nby * nbx;
   const int total = ntiles * splits;
   const int q = total / kNumXcd, rem = total % kNumXcd;
@@ -75,10 +89,10 @@ __device__ __forceinline__ void unit_of(int u, int nby, int nbx, int splits, int
     tn = t - tm * nbx;
     return;
   }
-  const int per_group = kGroupM * nbx;
+  const int per_group = gm * nbx;
   const int g = t / per_group;
-  const int first = g * kGroupM;
-  const int gsize = min(nby - first, kGroupM);
+  const int first = g * gm;
+  const int gsize = min(nby - first, gm);
   const int in = t - g * per_group;
   tm = first + in % gsize;
   tn = in / gsize;
