@@ -53,6 +53,17 @@ struct RowVec<float> {
   __device__ static float load1(const float* p) { return *p; }
 };
 
+// Row traffic is touched once: loads and stores stream past the caches (nontemporal).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_stream(uint4* p, const uint4& q) {
+  const u32x4_t v = {q.x, q.y, q.z, q.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Merge two (max, sum) pairs of the online softmax; a max of -inf marks an empty pair.
 __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
@@ -87,7 +98,9 @@ __device__ __forceinline__ void store_g8(const G8Out& go, int t, int i, const fl
   o.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(g[2], g[3], w, true);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(g[4], g[5], 0, false);
   o.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(g[6], g[7], w, true);
-  *reinterpret_cast<uint2*>(go.g8 + (int64_t)t * go.ldg + (int64_t)i * 8) = o;
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = {o.x, o.y};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(go.g8 + (int64_t)t * go.ldg + (int64_t)i * 8));
 }
 
 // Block-wide merge; every thread gets the row's (max, sum). Contains barriers.
@@ -165,7 +178,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
     for (int k = 0; k < VPT; ++k) {
       const int i = threadIdx.x + k * NT;
       if (i < nvec) {
-        RV::unpack(rowv[i], v[k]);
+        RV::unpack(ld_stream(rowv + i), v[k]);
         if ((i + 1) * E > P) {
 #pragma unroll
           for (int e = 0; e < E; ++e)
@@ -190,7 +203,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int i = threadIdx.x + k * NT;
-      q[k] = i < nvec ? rowv[i] : make_uint4(0, 0, 0, 0);
+      q[k] = i < nvec ? ld_stream(rowv + i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -262,7 +275,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
         }
       }
       if constexpr (G8) store_g8(go, t, i, g);
-      else rowv[i] = RV::pack(g);
+      else st_stream(rowv + i, RV::pack(g));
     }
   }
   if (threadIdx.x == 0) {
@@ -304,7 +317,7 @@ __global__ __launch_bounds__(256) void k_ce_rows_wave(TZ* __restrict__ Z, int64_
   for (int k = 0; k < VPT; ++k) {
     const int i = lane + k * kWave;
     if (i < nvec) {
-      RV::unpack(rowv[i], v[k]);
+      RV::unpack(ld_stream(rowv + i), v[k]);
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (i * E + e >= P) v[k][e] = -INFINITY;
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(256) void k_ce_rows_wave(TZ* __restrict__ Z, int64_
         }
       }
       if constexpr (G8) store_g8(go, t, i, g);
-      else rowv[i] = RV::pack(g);
+      else st_stream(rowv + i, RV::pack(g));
     }
   }
   if (lane == 0) {
@@ -395,7 +408,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
   float m = -INFINITY, s = 0.f;
   for (int i = threadIdx.x; i < nvec; i += NT) {
     float f[E];
-    RV::unpack(rowv[i], f);
+    RV::unpack(ld_stream(rowv + i), f);
     float cm = -INFINITY;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
   __syncthreads();  // zlab was read before any lane writes the row
   for (int i = threadIdx.x; i < nvec; i += NT) {
     float f[E];
-    RV::unpack(rowv[i], f);
+    RV::unpack(ld_stream(rowv + i), f);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = i * E + e;
@@ -428,7 +441,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
                    : 0.f;
     }
     if constexpr (G8) store_g8(go, t, i, f);
-    else rowv[i] = RV::pack(f);
+    else st_stream(rowv + i, RV::pack(f));
   }
   if (threadIdx.x == 0) {
     float l = 0.f;
