@@ -494,7 +494,9 @@ static void launch_ce_typed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
       hipLaunchKernelGGL((k_ce_rows_wave<TZ, 3, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
     else
       hipLaunchKernelGGL((k_ce_rows_wave<TZ, 4, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
-  } else if (nvec <= 256 * 16) {
+  } else if (nvec <= 256 * 8) {
+    // up to 8 vectors per lane on 256 lanes; longer rows take 512 lanes (P = 24576 bf16:
+    // 6 vectors per lane at 70 registers ran 16% faster than 12 at 99)
     launch_ce_nt<TZ, 256, G8>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse,
                               go, s);
   } else if (nvec <= 512 * 16) {
