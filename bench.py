@@ -67,10 +67,12 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload, stage):
+def recorded_traffic(workload, stage, e4m3=False):
     """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) recorded under profiles/
-    for this workload and stage, or None when absent or taken from other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    for this workload, operand type and stage, or None when absent or taken from other
+    kernel sources."""
+    name = f"{workload}_e4m3" if e4m3 else workload
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -198,12 +200,12 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_TFLOPS[ptype], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[ptype], 4),
-                "traffic": recorded_traffic(w.name, dom)}
+                "traffic": recorded_traffic(w.name, dom, e4m3)}
     else:
         achieved = amount / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic(w.name, dom)}
+                "traffic": recorded_traffic(w.name, dom, e4m3)}
 
     if args.calibrate_copy_mib:
         src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
