@@ -57,7 +57,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     off = align_up(off + bytes);
     return at;
   };
-  p.counters = take(kNumCounters * sizeof(int32_t));
+  p.counters = take(kCounterWords * sizeof(int32_t));
   p.vocab_pos = take((size_t)V * sizeof(int32_t));
   p.cand = take((size_t)(P > 0 ? P : 1) * sizeof(int32_t));
   p.tpos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
@@ -374,7 +374,7 @@ CePlan make_ce_plan(int64_t T) {
     return at;
   };
   const size_t n = (size_t)(T > 0 ? T : 1);
-  p.counters = take(kNumCounters * sizeof(int32_t));
+  p.counters = take(kCounterWords * sizeof(int32_t));
   p.tpos = take(n * sizeof(int32_t));
   p.ppos = take(n * sizeof(int32_t));
   p.row_loss = take(n * sizeof(float));

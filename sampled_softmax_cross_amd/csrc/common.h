@@ -15,8 +15,12 @@ enum Counter : int {
   kDistinct = 2,   // distinct targets
   kNextOffset = 3, // sweep offset after the build
   kCeDone = 4,     // CE rows finished (the last one reduces the loss)
-  kAmaxX = 5,      // e4m3 step: bf16 magnitude bits of max|x|
-  kNumCounters = 8
+  kNumCounters = 8,
+  // After the counters (not cleared with them): the e4m3 step's bf16 magnitude bits of
+  // max|x|, one partial per workgroup of the amax launch (at most kAmaxSlots).
+  kAmaxX = kNumCounters,
+  kAmaxSlots = 1024,
+  kCounterWords = kAmaxX + kAmaxSlots
 };
 constexpr int kDevTooManyTargets = 1;
 constexpr int kDevLabelRange = 2;

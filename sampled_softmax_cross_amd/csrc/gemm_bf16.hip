@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
     }
   }
   vm_wait<WAIT0>();
-  __syncthreads();
+  lds_barrier();
   read_frags(0, 0, 0);
 
   int g = 0;  // global stage index of this workgroup
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
       // of their fragment sets are in registers), so they take stages g + NSB (B) and
       // g + NS (A).
       vm_wait<WAIT>();
-      __syncthreads();
+      lds_barrier();
       if constexpr (NSB == NS) {
         issue_stage(g % NS);
       } else {
@@ -443,6 +443,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
     store_acc<OUT, TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow + l32, cc.n0 + bcol, lane >> 5,
                            OUT == kOutF32Split ? (cc.kb / kps) * split_stride : 0);
   }
+  // The ring's last loads (of stages past the last unit: zeros) land before the
+  // workgroup's LDS is released.
+  vm_wait_all();
 }
 
 #define SCE_GEMM_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL, EB)                 \

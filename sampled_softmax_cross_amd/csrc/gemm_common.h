@@ -39,6 +39,19 @@ __device__ __forceinline__ uint4 bload(rsrc_t r, int off) {
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for an LDS ring filled by buffer_load ... lds: this wave's LDS reads
+// complete (lgkmcnt 0), then s_barrier. Each wave waits for its own loads into the ring
+// (vmcnt) before calling it. A fenced __syncthreads would also wait for every
+// outstanding load and store of the wave (vmcnt 0: the loads write LDS), which empties
+// a ring meant to keep stages in flight across the barrier. The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 enum OutMode { kOutBF16 = 0, kOutF32 = 1, kOutF32Split = 2 };
 
 // Output tile of workgroup `bid` among nby x nbx tiles: XCD-contiguous, grouped.
