@@ -32,11 +32,12 @@ int64_t mod64(int64_t a, int64_t m) {
 struct Plan {
   int64_t Peff = 0, ldz = 0;
   int64_t ldwc = 0;   // row pitch of the gathered W_C (elements)
+  int64_t ldt = 0;    // bf16: row pitch of W_C's transpose [d, P_eff] (elements)
   int64_t ldg = 0;    // e4m3 step: row pitch of the e4m3 gradient (bytes)
   int splits = 1;     // k-split of the dW product (fp32 partials reduced by the scatter)
   int dx_splits = 1;  // k-split of the dX product (fp32 partials reduced into dX)
   size_t counters = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
-  size_t wc = 0, z = 0, part = 0, total = 0;
+  size_t wc = 0, wt = 0, z = 0, part = 0, total = 0;
   size_t x8 = 0, g8 = 0, scales = 0;  // e4m3 step
 };
 
@@ -68,6 +69,12 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     // bf16: 1536 B), the logits product measured 15% slower on unpadded rows.
     p.ldwc = P > 0 ? d + 64 : d;
     p.wc = take(P > 0 ? (size_t)P * p.ldwc * ws : 0);
+    if (dtype == SCE_BF16) {
+      // The dX product's B operand: W_C transposed (W itself at P = 0), k contiguous,
+      // rows a multiple of 16 bytes with zeros past P_eff.
+      p.ldt = round_up(p.Peff, 8);
+      p.wt = take((size_t)d * p.ldt * ws);
+    }
     p.z = take((size_t)T * p.ldz * (e4m3 ? 2 : es));
     if (e4m3) {
       p.ldg = p.ldz;
@@ -227,12 +234,17 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   void* Z = ws + p.z;
   float* part = reinterpret_cast<float*>(ws + p.part);
   const void* WC = P > 0 ? static_cast<const void*>(ws + p.wc) : W;
+  // dX's B operand: bf16 reads the transposed copy (r-major), f32 W_C itself (k-major)
+  const void* dxB = bf16 ? static_cast<const void*>(ws + p.wt) : WC;
+  const int64_t dxldb = bf16 ? p.ldt : p.ldwc;
 
   StageMarks marks(hs);
   marks.mark(SCE_STAGE_CANDIDATES);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
                                    (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
                                    W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), hs);
+  if (e == hipSuccess && bf16 && T > 0)
+    e = launch_transpose(WC, p.ldwc, (int)p.Peff, (int)d, 2, ws + p.wt, p.ldt, hs);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
     GemmArgs g{x, d, WC, p.ldwc, Z, p.ldz, T, p.Peff, d, 1, 0};
@@ -245,10 +257,10 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   marks.mark(SCE_STAGE_DX);
   if (e == hipSuccess && T > 0) {
     if (p.dx_splits > 1) {
-      GemmArgs g{Z, p.ldz, WC, p.ldwc, part, d, T, d, p.Peff, p.dx_splits, T * d};
+      GemmArgs g{Z, p.ldz, dxB, dxldb, part, d, T, d, p.Peff, p.dx_splits, T * d};
       e = launch_gemm(Gemm::DX, bf16, g, hs);
     } else {
-      GemmArgs g{Z, p.ldz, WC, p.ldwc, dX, d, T, d, p.Peff, 1, 0};
+      GemmArgs g{Z, p.ldz, dxB, dxldb, dX, d, T, d, p.Peff, 1, 0};
       e = launch_gemm(Gemm::DX, bf16, g, hs);
     }
   }

@@ -453,10 +453,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
       const void*, int64_t, const void*, int64_t, void*, int64_t, int64_t, int64_t, int64_t,     \
       int64_t, int64_t, int, const float*);
 SCE_GEMM_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2, true, 2)
-SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 64, 2, false, 2)
-SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2, false, 2)
-SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutBF16, 3, 2, 32, 3, true, 2)
-SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutF32Split, 3, 2, 32, 3, true, 2)
+SCE_GEMM_INST(256, 192, 4, 2, false, false, kOutBF16, 2, 1, 64, 2, true, 2)
+SCE_GEMM_INST(256, 192, 4, 2, false, false, kOutF32Split, 2, 1, 64, 2, true, 2)
+SCE_GEMM_INST(128, 256, 2, 4, false, false, kOutBF16, 3, 2, 32, 3, true, 2)
+SCE_GEMM_INST(128, 256, 2, 4, false, false, kOutF32Split, 3, 2, 32, 3, true, 2)
 SCE_GEMM_INST(256, 256, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false, 2)
 SCE_GEMM_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 128, 2, true, 1)
 SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 128, 2, false, 1)
@@ -495,7 +495,13 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
 //    stages would fetch half cache lines);
 //  * dX, N a multiple of 192: 256 x 192 tiles, 8 waves (4 x 2, 64 x 96 each), one
 //    workgroup per CU, two stages of 64 k: N = 768 gives 4 column tiles, so M = 16384
-//    fills the 256 CUs exactly once;
+//    fills the 256 CUs exactly once. bf16: B is the transposed copy of W_C ([d, P], k
+//    contiguous), so both operands are r-major and every fragment is read with
+//    ds_read_b128 (against W_C read k-major through transposing LDS reads: 11% faster
+//    in the step at T = 16384, P = 10240, 12% at T = 49152, P = 24576; the copy costs
+//    7 us at the first). e4m3 reads W_C k-major (ds_read_b64_tr_b8): there the r-major
+//    operand measured 2-4% faster alone and no faster in the step once its copy is
+//    counted;
 //  * dX otherwise: 128 x 256 tiles with two workgroups per CU (their epilogues and
 //    barrier stalls interleave), three stages of 32 k, 8 waves of 64 x 64;
 //  * dW: 256 x 256 tiles, 8 waves (4 x 2, 64 x 128 each), two stages of 64 k, fragment
@@ -586,11 +592,11 @@ hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
     case Gemm::DX:
       if (dx_wide(a.N))
         return a.splits > 1
-                   ? run16<kWideM, kWideN, 4, 2, false, true, kOutF32Split, 2, 1, 64, 2, false>(a, s)
-                   : run16<kWideM, kWideN, 4, 2, false, true, kOutBF16, 2, 1, 64, 2, false>(a, s);
+                   ? run16<kWideM, kWideN, 4, 2, false, false, kOutF32Split, 2, 1, 64, 2, true>(a, s)
+                   : run16<kWideM, kWideN, 4, 2, false, false, kOutBF16, 2, 1, 64, 2, true>(a, s);
       return a.splits > 1
-                 ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 3, kOcc, 32, 3, true>(a, s)
-                 : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 3, kOcc, 32, 3, true>(a, s);
+                 ? run16<kTileM, kTileN, 2, 4, false, false, kOutF32Split, 3, kOcc, 32, 3, true>(a, s)
+                 : run16<kTileM, kTileN, 2, 4, false, false, kOutBF16, 3, kOcc, 32, 3, true>(a, s);
     case Gemm::DW: return run16<kDwM, kDwN, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false>(a, s);
   }
   return hipErrorInvalidValue;

@@ -70,6 +70,12 @@ hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stri
 hipError_t launch_ce_prep(const int32_t* tpos_in, const int32_t* ppos_in, int T, int P,
                           int32_t* tpos, int32_t* ppos, int32_t* counters, hipStream_t s);
 // out[i, :] = W[idx[i], :] (zeros and kDevLabelRange in *status for idx outside [0, V)).
+// dst[c, r] = src[r, c] for r < rows, c < cols, elements of es bytes (1 or 2); dst
+// columns r in [rows, ld_dst) are written as zeros. src rows are ld_src elements apart,
+// dst rows ld_dst; both pitches and cols keep every 16-byte chunk whole (multiples of
+// 16 / es).
+hipError_t launch_transpose(const void* src, int64_t ld_src, int rows, int cols, int es, void* dst,
+                            int64_t ld_dst, hipStream_t s);
 hipError_t launch_gather_checked(const void* W, int64_t V, const int32_t* idx, int n,
                                  int row_bytes, void* out, int64_t out_row_bytes,
                                  int32_t* status, hipStream_t s);
