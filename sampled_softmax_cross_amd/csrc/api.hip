@@ -192,7 +192,7 @@ sce_status sce_build_candidates(const int64_t* targets, const int64_t* prefix_ta
   int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
                                    (int)mod64(offset, V), counters, candidates_out, vocab_pos,
-                                   target_pos_out, ppos, nullptr, 0, nullptr, 0, hs);
+                                   target_pos_out, ppos, nullptr, 0, nullptr, 0, nullptr, 0, hs);
   if (e == hipSuccess && aux_out) e = launch_write_aux(counters, aux_out, hs);
   return hip_status(e);
 }
@@ -242,7 +242,8 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   marks.mark(SCE_STAGE_CANDIDATES);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
                                    (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
-                                   W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), hs);
+                                   W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), dW,
+                                   (int)(d * es), hs);
   if (e == hipSuccess && bf16 && T > 0)
     e = launch_transpose(WC, p.ldwc, (int)p.Peff, (int)d, 2, ws + p.wt, p.ldt, hs);
   marks.mark(SCE_STAGE_LOGITS);
@@ -266,8 +267,8 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   }
   marks.mark(SCE_STAGE_DX_REDUCE);
   if (e == hipSuccess && T > 0 && p.dx_splits > 1)
-    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, nullptr, (int)T, (int)T, (int)d,
-                            bf16, dX, nullptr, hs);
+    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, bf16, dX, nullptr,
+                            hs);
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess) {
     GemmArgs g{Z, p.ldz, x, d, part, d, p.Peff, d, T, p.splits, p.Peff * d};
@@ -275,10 +276,11 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   }
   marks.mark(SCE_STAGE_SCATTER);
   if (e == hipSuccess) {
-    // The dense scatter is the last launch; its extra block also finishes the loss.
+    // The candidate rows of dW (the others were cleared by the remap launch); the
+    // launch's extra block also finishes the loss.
     const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
-    e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? vocab_pos : nullptr,
-                            P > 0 ? cand : nullptr, (int)p.Peff, (int)V, (int)d, bf16, dW, &fin, hs);
+    e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? cand : nullptr, (int)p.Peff,
+                            (int)d, bf16, dW, &fin, hs);
   }
   marks.mark(SCE_NUM_STAGES);
   return hip_status(e);
@@ -328,7 +330,7 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   marks.mark(SCE_STAGE_CANDIDATES);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
                                    (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
-                                   W8, (int)d, ws + p.wc, (int)p.ldwc, hs);
+                                   W8, (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2), hs);
   if (e == hipSuccess) e = launch_quant_x(x, T * d, counters, w_scale, x8, scales, scales_out, hs);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
@@ -353,8 +355,8 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   }
   marks.mark(SCE_STAGE_DX_REDUCE);
   if (e == hipSuccess && T > 0 && p.dx_splits > 1)
-    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, nullptr, (int)T, (int)T, (int)d,
-                            true, dX, nullptr, hs);
+    e = launch_scatter_rows(part, p.dx_splits, T * d, nullptr, (int)T, (int)d, true, dX, nullptr,
+                            hs);
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess && T > 0) {
     GemmArgs g{g8, p.ldg, x8, d, part, d, p.Peff, d, T, p.splits, p.Peff * d, scales + kScaleDw};
@@ -363,9 +365,10 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   marks.mark(SCE_STAGE_SCATTER);
   if (e == hipSuccess) {
     const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
-    // T = 0: no product ran; the scatter's zero blocks still clear every row of dW.
-    e = launch_scatter_rows(part, T > 0 ? p.splits : 0, p.Peff * d, P > 0 ? vocab_pos : nullptr,
-                            P > 0 ? cand : nullptr, (int)p.Peff, (int)V, (int)d, true, dW, &fin, hs);
+    // T = 0: no product ran; the candidate rows are written as zeros (a sum over no
+    // partials), the others were cleared by the remap launch.
+    e = launch_scatter_rows(part, T > 0 ? p.splits : 0, p.Peff * d, P > 0 ? cand : nullptr,
+                            (int)p.Peff, (int)d, true, dW, &fin, hs);
   }
   marks.mark(SCE_NUM_STAGES);
   return hip_status(e);
@@ -427,7 +430,7 @@ sce_status sce_ce_rows(void* Z, int64_t ldz, int64_t T, int64_t P, int dtype,
   if (e == hipSuccess) {
     // the scatter launch with no rows: only its loss block runs
     const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
-    e = launch_scatter_rows(nullptr, 0, 0, nullptr, nullptr, 0, 0, 8, bf16, nullptr, &fin, hs);
+    e = launch_scatter_rows(nullptr, 0, 0, nullptr, 0, 8, bf16, nullptr, &fin, hs);
   }
   return hip_status(e);
 }

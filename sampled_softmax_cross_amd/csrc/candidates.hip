@@ -191,13 +191,20 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
 }
 
 // Blocks [0, remap_blocks): labels -> positions in C (identity when P == 0), count N.
-// Blocks after that: the row gather W_C = W[C] (none when P == 0).
+// The next gather_blocks: the row gather W_C = W[C] (none when P == 0). The rest: the
+// rows of the dense gradient outside C set to zero (written here, while the memory
+// system is otherwise idle, rather than beside the candidate rows at the end of the
+// step).
 __global__ __launch_bounds__(256) void k_remap_gather(
     const int64_t* __restrict__ targets, const int64_t* __restrict__ prefix, int T, int V, int P,
     const int32_t* __restrict__ vocab_pos, int32_t* __restrict__ target_pos,
     int32_t* __restrict__ prefix_pos, int32_t* __restrict__ counters, int remap_blocks,
     const uint4* __restrict__ W, const int32_t* __restrict__ C, int row_vecs,
-    uint4* __restrict__ WC, int wc_vecs) {
+    uint4* __restrict__ WC, int wc_vecs, int gather_blocks, uint4* __restrict__ dW, int dw_vecs) {
+  if ((int)blockIdx.x >= remap_blocks + gather_blocks) {
+    zero_rows_block((int)blockIdx.x - remap_blocks - gather_blocks, vocab_pos, V, dw_vecs, dW);
+    return;
+  }
   if ((int)blockIdx.x >= remap_blocks) {
     gather_rows_block((int)blockIdx.x - remap_blocks, W, C, P, row_vecs, WC, wc_vecs);
     return;
@@ -236,19 +243,21 @@ __global__ void k_write_aux(const int32_t* __restrict__ counters, int64_t* __res
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
                              int stride, int off, int32_t* counters, int32_t* C,
                              int32_t* vocab_pos, int32_t* target_pos, int32_t* prefix_pos,
-                             const void* W, int row_bytes, void* WC, int wc_row_bytes,
-                             hipStream_t s) {
+                             const void* W, int row_bytes, void* WC, int wc_row_bytes, void* dW,
+                             int dw_row_bytes, hipStream_t s) {
   const bool mark_lds = V <= kMaxBitmapClasses;
   const size_t lds = mark_lds ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
   hipLaunchKernelGGL(k_cand, dim3(1), dim3(kBuildThreads), lds, s, targets, prefix, T, V, P,
                      stride, off, mark_lds, C, vocab_pos, counters);
   const int remap_blocks = (T + 255) / 256;
   const int gather_blocks = (W != nullptr && P > 0) ? gather_block_count(P, row_bytes / 16) : 0;
-  if (remap_blocks + gather_blocks > 0)
-    hipLaunchKernelGGL(k_remap_gather, dim3(remap_blocks + gather_blocks), dim3(256), 0, s,
-                       targets, prefix, T, V, P, vocab_pos, target_pos, prefix_pos, counters,
+  const int zero_blocks = (dW != nullptr && P > 0) ? zero_block_count(V, dw_row_bytes / 16) : 0;
+  if (remap_blocks + gather_blocks + zero_blocks > 0)
+    hipLaunchKernelGGL(k_remap_gather, dim3(remap_blocks + gather_blocks + zero_blocks), dim3(256),
+                       0, s, targets, prefix, T, V, P, vocab_pos, target_pos, prefix_pos, counters,
                        remap_blocks, reinterpret_cast<const uint4*>(W), C, row_bytes / 16,
-                       reinterpret_cast<uint4*>(WC), wc_row_bytes / 16);
+                       reinterpret_cast<uint4*>(WC), wc_row_bytes / 16, gather_blocks,
+                       reinterpret_cast<uint4*>(dW), dw_row_bytes / 16);
   return hipGetLastError();
 }
 

@@ -51,13 +51,12 @@ __device__ void finish_loss(const LossOut& f) {
   }
 }
 
-// One launch, three roles by block index:
+// One launch, two roles by block index:
 //  * with a LossOut, block 0 finishes the loss;
-//  * zero blocks clear every dW row that is not a candidate (vocab_pos < 0): one
-//    lookup per vector, then stores only;
 //  * row blocks write the candidate rows: dW[C[p], :] = sum over splits of
 //    part[s, p, :], with C = identity when no map is given. Their loads depend on
 //    nothing, the candidate's class only addresses the store.
+// (The rows outside C are cleared earlier, by the label-remap launch.)
 // Each lane handles kScatterVecs vectors of 8 consecutive elements, a block apart,
 // every load issued before the first store. Flat vector indexes fit 32 bits: V * d / 8
 // and T * d / 8 are at most 2^31 by the library's size limits.
@@ -82,33 +81,17 @@ __device__ __forceinline__ void store_vec(void* dW, size_t i, const float4& lo, 
 
 template <bool BF16>
 __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
-    const float* __restrict__ part, int splits, int64_t split_stride,
-    const int32_t* __restrict__ vocab_pos, const int32_t* __restrict__ C, int rows, int V, int d,
-    void* __restrict__ dW, int zero_blocks, int row_blocks, LossOut fin) {
-  const int first = (int)gridDim.x - zero_blocks - row_blocks;  // 1 with a LossOut, else 0
+    const float* __restrict__ part, int splits, int64_t split_stride, const int32_t* __restrict__ C,
+    int rows, int d, void* __restrict__ dW, int row_blocks, LossOut fin) {
+  const int first = (int)gridDim.x - row_blocks;  // 1 with a LossOut, else 0
   const int b = (int)blockIdx.x - first;
   if (b < 0) {
     finish_loss(fin);
     return;
   }
   const uint32_t vpr = (uint32_t)d / 8;
-  if (b < zero_blocks) {
-    const uint32_t total = (uint32_t)V * vpr;
-    const uint32_t i0 = (uint32_t)b * kPerBlock + threadIdx.x;
-    int pos[kScatterVecs];
-#pragma unroll
-    for (int u = 0; u < kScatterVecs; ++u) {
-      const uint32_t i = i0 + u * kCopyThreads;
-      pos[u] = i < total ? vocab_pos[i / vpr] : 0;
-    }
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int u = 0; u < kScatterVecs; ++u)
-      if (pos[u] < 0) store_vec<BF16>(dW, i0 + u * kCopyThreads, z, z);
-    return;
-  }
   const uint32_t total = (uint32_t)rows * vpr;
-  const uint32_t i0 = (uint32_t)(b - zero_blocks) * kPerBlock + threadIdx.x;
+  const uint32_t i0 = (uint32_t)b * kPerBlock + threadIdx.x;
   float4 lo[kScatterVecs], hi[kScatterVecs];
 #pragma unroll
   for (int u = 0; u < kScatterVecs; ++u) {
@@ -237,21 +220,19 @@ hipError_t launch_transpose(const void* src, int64_t ld_src, int rows, int cols,
 }
 
 hipError_t launch_scatter_rows(const float* part, int splits, int64_t split_stride,
-                               const int32_t* vocab_pos, const int32_t* C, int rows, int V, int d,
-                               bool bf16, void* dW, const LossOut* fin, hipStream_t s) {
+                               const int32_t* C, int rows, int d, bool bf16, void* dW,
+                               const LossOut* fin, hipStream_t s) {
   const int64_t vpr = d / 8;
-  const int zero_blocks = vocab_pos ? (int)(((int64_t)V * vpr + kPerBlock - 1) / kPerBlock) : 0;
   const int row_blocks = (int)(((int64_t)rows * vpr + kPerBlock - 1) / kPerBlock);
   const LossOut f = fin ? *fin : LossOut{nullptr, 0, nullptr, nullptr, nullptr};
-  const int grid = zero_blocks + row_blocks + (fin ? 1 : 0);
+  const int grid = row_blocks + (fin ? 1 : 0);
   if (grid > 0) {
     if (bf16)
       hipLaunchKernelGGL(k_scatter_rows<true>, dim3(grid), dim3(kCopyThreads), 0, s, part, splits,
-                         split_stride, vocab_pos, C, rows, V, d, dW, zero_blocks, row_blocks, f);
+                         split_stride, C, rows, d, dW, row_blocks, f);
     else
       hipLaunchKernelGGL(k_scatter_rows<false>, dim3(grid), dim3(kCopyThreads), 0, s, part,
-                         splits, split_stride, vocab_pos, C, rows, V, d, dW, zero_blocks,
-                         row_blocks, f);
+                         splits, split_stride, C, rows, d, dW, row_blocks, f);
   }
   return hipGetLastError();
 }
