@@ -36,7 +36,7 @@ struct Plan {
   int64_t ldg = 0;    // e4m3 step: row pitch of the e4m3 gradient (bytes)
   int splits = 1;     // k-split of the dW product (fp32 partials reduced by the scatter)
   int dx_splits = 1;  // k-split of the dX product (fp32 partials reduced into dX)
-  size_t counters = 0, vocab_pos = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
+  size_t counters = 0, bits = 0, wpre = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
   size_t wc = 0, wt = 0, z = 0, part = 0, total = 0;
   size_t x8 = 0, g8 = 0, scales = 0;  // e4m3 step
 };
@@ -59,7 +59,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     return at;
   };
   p.counters = take(kCounterWords * sizeof(int32_t));
-  p.vocab_pos = take((size_t)V * sizeof(int32_t));
+  p.bits = take((size_t)((V + 31) / 32) * sizeof(uint32_t));
+  p.wpre = take((size_t)((V + 31) / 32) * sizeof(int32_t));
   p.cand = take((size_t)(P > 0 ? P : 1) * sizeof(int32_t));
   p.tpos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
   p.ppos = take((size_t)(T > 0 ? T : 1) * sizeof(int32_t));
@@ -188,11 +189,13 @@ sce_status sce_build_candidates(const int64_t* targets, const int64_t* prefix_ta
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
-  int32_t* vocab_pos = vocab_pos_out ? vocab_pos_out : reinterpret_cast<int32_t*>(ws + p.vocab_pos);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
   int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), counters, candidates_out, vocab_pos,
-                                   target_pos_out, ppos, nullptr, 0, nullptr, 0, nullptr, 0, hs);
+                                   (int)mod64(offset, V), counters, candidates_out, bits, wpre,
+                                   vocab_pos_out, target_pos_out, ppos, nullptr, 0, nullptr, 0,
+                                   nullptr, 0, hs);
   if (e == hipSuccess && aux_out) e = launch_write_aux(counters, aux_out, hs);
   return hip_status(e);
 }
@@ -226,7 +229,8 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
-  int32_t* vocab_pos = reinterpret_cast<int32_t*>(ws + p.vocab_pos);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
   int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
   int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
   int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
@@ -241,7 +245,8 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
   StageMarks marks(hs);
   marks.mark(SCE_STAGE_CANDIDATES);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
+                                   (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
+                                   tpos, ppos,
                                    W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), dW,
                                    (int)(d * es), hs);
   if (e == hipSuccess && bf16 && T > 0)
@@ -314,7 +319,8 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
-  int32_t* vocab_pos = reinterpret_cast<int32_t*>(ws + p.vocab_pos);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
   int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
   int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
   int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
@@ -329,7 +335,8 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   StageMarks marks(hs);
   marks.mark(SCE_STAGE_CANDIDATES);
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), counters, cand, vocab_pos, tpos, ppos,
+                                   (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
+                                   tpos, ppos,
                                    W8, (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2), hs);
   if (e == hipSuccess) e = launch_quant_x(x, T * d, counters, w_scale, x8, scales, scales_out, hs);
   marks.mark(SCE_STAGE_LOGITS);

@@ -10,15 +10,16 @@ constexpr int kBuildThreads = 1024;
 // Largest vocabulary whose candidate bitmaps (2 x V bits) the build keeps in LDS.
 constexpr int kMaxBitmapClasses = 131072;
 
-// Candidate build (P > 0) or label check (P == 0), then the label remap and, when W
-// is given and P > 0, the row gather W_C = W[C] (rows of row_bytes, a multiple of 16)
-// and, when dW is given and P > 0, the rows of the dense gradient outside C set to zero
-// (rows of dw_row_bytes, a multiple of 16).
+// Candidate build (P > 0: C, and the candidate bitmap `bits` and per-word prefix
+// counts `wpre`, ceil(V/32) words each) or label check (P == 0), then the label remap
+// and, when P > 0: with W, the row gather W_C = W[C] (rows of row_bytes, a multiple of
+// 16); with dW, the rows of the dense gradient outside C set to zero (rows of
+// dw_row_bytes, a multiple of 16); with vocab_pos, the class -> position map.
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
-                             int stride, int off, int32_t* counters, int32_t* C,
-                             int32_t* vocab_pos, int32_t* target_pos, int32_t* prefix_pos,
-                             const void* W, int row_bytes, void* WC, int wc_row_bytes, void* dW,
-                             int dw_row_bytes, hipStream_t s);
+                             int stride, int off, int32_t* counters, int32_t* C, uint32_t* bits,
+                             int32_t* wpre, int32_t* vocab_pos, int32_t* target_pos,
+                             int32_t* prefix_pos, const void* W, int row_bytes, void* WC,
+                             int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s);
 hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s);
 
 // Row gather, one block of 256 lanes per kGatherRows rows: 32 lanes per row, each
@@ -52,25 +53,26 @@ __device__ __forceinline__ void gather_rows_block(int blk, const uint4* __restri
   }
 }
 // Zero rows of the dense gradient: block `blk` covers kZeroVecs 16-byte vectors of the
-// flat [V, vpr] array (vpr vectors per row) and clears those of rows outside C
-// (vocab_pos < 0): one lookup per vector, then stores only.
+// flat [V, vpr] array (vpr vectors per row) and clears those of rows outside C (bit
+// clear in the candidate bitmap): one lookup per vector, then stores only.
 constexpr int kZeroVecs = 256 * 4;
 inline int zero_block_count(int V, int vpr) {
   return (int)(((int64_t)V * vpr + kZeroVecs - 1) / kZeroVecs);
 }
-__device__ __forceinline__ void zero_rows_block(int blk, const int32_t* __restrict__ vocab_pos,
-                                                int V, int vpr, uint4* __restrict__ dW) {
+__device__ __forceinline__ void zero_rows_block(int blk, const uint32_t* __restrict__ bits, int V,
+                                                int vpr, uint4* __restrict__ dW) {
   const int64_t total = (int64_t)V * vpr;
   const int64_t i0 = (int64_t)blk * kZeroVecs + threadIdx.x;
-  int pos[4];
+  bool in_c[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t i = i0 + u * 256;
-    pos[u] = i < total ? vocab_pos[i / vpr] : 0;
+    const int row = i < total ? (int)(i / vpr) : 0;
+    in_c[u] = i >= total || ((bits[row >> 5] >> (row & 31)) & 1u);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    if (pos[u] < 0) dW[i0 + u * 256] = make_uint4(0, 0, 0, 0);
+    if (!in_c[u]) dW[i0 + u * 256] = make_uint4(0, 0, 0, 0);
 }
 // dW[C[p], :] = sum over splits of part[s, p, :] (fp32) in dtype for p < rows (C null:
 // the identity). When `fin` is given, the launch also finishes the step's scalars:
