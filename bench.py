@@ -44,9 +44,9 @@ def stage_work(w, P_eff, e4m3=False):
         "dx": ("mfma", flops),
         "dw": ("mfma", flops),
         "ce": ("hbm", ce_bytes),
-
-        # read the fp32 candidate-row gradient once, write the dense dW, read vocab_pos
-        "scatter": ("hbm", P_eff * w.d * 4.0 + w.V * w.d * es + 4 * w.V),
+        # read the fp32 candidate-row gradient once, write the candidate rows of dense dW
+        # (the rows outside C are cleared in the candidates stage)
+        "scatter": ("hbm", P_eff * w.d * (4.0 + (2 if e4m3 else es))),
         # sum the fp32 k-split partials of dX into dX (bytes of a 2-way split)
         "dx_reduce": ("hbm", 2 * w.T * w.d * 4.0 + w.T * w.d * es),
     }
