@@ -89,6 +89,11 @@ def test_device_detected_errors():
     y = np.arange(10, dtype=np.int64)
     g = _run(V, 9, 3, 0, y, None)       # 10 distinct targets > P = 9
     assert g["aux"][3] & binding.DEV_TOO_MANY_TARGETS
+    # the map left behind keeps every later access in bounds: C = [0, P), positions
+    # of the first P classes, -1 elsewhere
+    assert np.array_equal(g["C"], np.arange(9))
+    assert np.array_equal(g["vocab_pos"], np.where(np.arange(V) < 9, np.arange(V), -1))
+    assert np.array_equal(g["target_pos"], np.where(y < 9, y, -1))
     g = _run(V, 20, 3, 0, np.array([1, 100], dtype=np.int64), None)
     assert g["aux"][3] & binding.DEV_LABEL_RANGE
     g = _run(V, 20, 3, 0, np.array([1, 2], dtype=np.int64), np.array([-2, 5], dtype=np.int64))
