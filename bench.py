@@ -94,6 +94,8 @@ def main():
                          "operand step on the same bf16 microbatch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the measured reference peaks (device copy, library GEMM)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--micro", choices=["softmax", "gather"], default=None,
                     help="instead of the step: time one building block on its own over the "
@@ -216,6 +218,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    achievable = None if args.no_achievable else measured_peaks(torch, dev, ptype)
+    if achievable:
+        ref = achievable["gemm_tflops"] if kind == "mfma" else achievable["copy_gbs"]
+        achievable["dominant_frac"] = round(roof["achieved"] / ref, 4)
+        log(f"[bench] achievable on this GPU: {achievable}")
+
     full_cmp = None
     if not args.no_full_compare and w.P > 0:
         ms_v, _ = timed(w.V, max(5, args.steps // 5), 2)
@@ -247,11 +255,42 @@ def main():
                    "prefix_targets": w.prefix,
                    **({"operands": "e4m3 x and lm_head, bf16 logits"} if e4m3 else {})},
         "roofline": roof,
+        "achievable": achievable,
         "stages": stages,
         "full_softmax_same_library": full_cmp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_peaks(torch, dev, ptype):
+    """Reference rates measured on this GPU beside the published peaks: a 1 GiB
+    device-to-device copy (bytes read + written per second) and the vendor library's
+    dense product at 8192^3 in the step's product type (hipBLASLt through torch;
+    e4m3 through torch._scaled_mm with unit scales, f32 through torch.matmul)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    copy_ms = _time_ms(lambda: dst.copy_(src), reps=20, warmup=3)
+    del src, dst
+    m = 8192
+    if ptype == "e4m3":
+        a = torch.randn(m, m, device=dev).to(torch.float8_e4m3fn)
+        b = torch.randn(m, m, device=dev).to(torch.float8_e4m3fn).t()  # k-contiguous columns
+        one = torch.tensor(1.0, device=dev)
+        fn = lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+    else:
+        dt = torch.bfloat16 if ptype == "bf16" else torch.float32
+        a = torch.randn(m, m, device=dev, dtype=dt)
+        b = torch.randn(m, m, device=dev, dtype=dt)
+        fn = lambda: torch.matmul(a, b)
+    gemm_ms = _time_ms(fn, reps=10, warmup=3)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2.0 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "gemm_tflops": round(2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm": f"{m}^3 {ptype}, vendor library"}
 
 
 def _time_ms(fn, reps=50, warmup=10):
