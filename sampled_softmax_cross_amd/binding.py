@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(PKG, "libsampledce.so")
 
 SCE_F32, SCE_BF16, SCE_E4M3 = 0, 1, 2
 DEV_TOO_MANY_TARGETS, DEV_LABEL_RANGE, DEV_SCALE_RANGE = 1, 2, 4
+# size limits (SCE_MAX_V_SAMPLED, SCE_MAX_V, SCE_MAX_D of include/sampled_ce.h)
+MAX_V_SAMPLED, MAX_V, MAX_D = 131072, 1048576, 16384
 STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
 
 EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sampled_ce_forward_backward",

@@ -31,6 +31,15 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_binding_constants_match_the_header():
+    src = open(os.path.join(ROOT, "include", "sampled_ce.h")).read()
+    define = lambda name: int(re.search(rf"#define\s+{name}\s+\(?(\d+)", src).group(1))
+    assert binding.MAX_V_SAMPLED == define("SCE_MAX_V_SAMPLED")
+    assert binding.MAX_V == define("SCE_MAX_V")
+    assert binding.MAX_D == define("SCE_MAX_D")
+    assert binding.DEV_SCALE_RANGE == define("SCE_DEV_SCALE_RANGE")
+
+
 def test_version_and_status_strings(lib):
     assert lib.sce_abi_version() == 1
     for code in range(4):
