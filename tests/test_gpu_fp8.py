@@ -22,6 +22,10 @@ CASES = [
     (64, 768, 50304, 10240, True, 0.0, 20011),  # full vocabulary and hidden size
     (2050, 96, 2500, 1601, False, 0.0, 3),
     (1, 64, 100, 40, True, 0.0, 3),             # one token
+    # the size limits of include/sampled_ce.h
+    (64, 64, 131072, 40000, True, 0.0, 99991),  # V = SCE_MAX_V_SAMPLED
+    (48, 64, 1048576, 0, True, 0.0, 1),         # V = SCE_MAX_V: rows for the streaming CE
+    (40, 16384, 600, 200, True, 0.0, 7),        # d = SCE_MAX_D
 ]
 
 
@@ -57,7 +61,9 @@ def test_fp8_step_matches_oracle(T, d, V, P, prefix, ign, stride):
     assert np.array_equal(out["target_pos"].cpu().numpy(), cand["target_pos"])
     assert np.array_equal(out["prefix_pos"].cpu().numpy(), cand["prefix_pos"])
     aux = out["aux"].cpu().numpy()
-    assert aux.tolist() == [cand["num_targets"], cand["N"], cand["next_offset"] if P else offset, 0]
+    # the distinct count is not formed above the sampled path's bitmap limit (full softmax)
+    distinct = -1 if P == 0 and V > binding.MAX_V_SAMPLED else cand["num_targets"]
+    assert aux.tolist() == [distinct, cand["N"], cand["next_offset"] if P else offset, 0]
     sx, sg = out["scales"].cpu().numpy().astype(np.float64)
     assert (sx, sg) == (ref["s_x"], ref["s_g"])
     # floating point: within the derived bounds
