@@ -19,8 +19,9 @@
 //    read with ds_read_b64_tr_b16: within each 16-lane group, lane j receives element i
 //    from the address supplied by lane 4i + j/4 (at element offset j % 4), so lanes
 //    that point at rows k..k+3 and 4-column groups assemble 8-k fragments of single
-//    columns. e4m3: chunks XOR-swizzled by k & 7 (rows of a multiple of 128 bytes) or
-//    (k >> 1) & 3 (192-byte rows); ds_read_b64_tr_b8 gives lane j byte i from the
+//    columns. e4m3: chunks XOR-swizzled by 2 * (k & 7) (rows of a multiple of 256
+//    bytes), k & 7 (128-byte rows) or (k >> 1) & 3 (192-byte rows);
+//    ds_read_b64_tr_b8 gives lane j byte i from the
 //    address of lane 2i + j/8 (at byte offset j % 8): lanes pointing at rows k..k+7 and
 //    8-column groups assemble 8-k pieces of single columns, four of which make a
 //    32-k fragment.
@@ -75,16 +76,21 @@ __device__ __forceinline__ int rm_index(int row, int ch) {
 // land on distinct bank groups. bf16 reads touch rows k..k+3 with 8 bytes each per
 // lane quad: rows of a multiple of 256 bytes start on the same banks, so they shift by
 // 4 * (k & 3) chunks; 384-byte rows alternate between two bank offsets, so rows k and
-// k + 2 shift by 4 chunks. e4m3 reads touch rows k..k+7, 16 bytes each: rows of a
-// multiple of 128 bytes shift by k & 7 chunks; 192-byte rows alternate between two
-// offsets 64 bytes apart, so rows k, k + 2, k + 4, k + 6 shift by (k >> 1) & 3.
+// k + 2 shift by 4 chunks. e4m3 reads touch rows k..k+7 and two adjacent chunks, 16
+// bytes each: with rows of a multiple of 256 bytes (all on the same banks), rows shift
+// by 2 * (k & 7) chunks, so the two chunks land on disjoint halves of the 16 groups
+// of four banks (k & 7 kept both within the same 8 groups: half of the LDS cycles of
+// the 256-wide e4m3 tiles were bank conflicts, counted by SQ_LDS_BANK_CONFLICT; none
+// now); rows of 128 bytes shift by k & 7; 192-byte rows alternate between two offsets
+// 64 bytes apart, so rows k, k + 2, k + 4, k + 6 shift by (k >> 1) & 3.
 template <int RB, int EB>
 __device__ __forceinline__ int km_swizzle(int k) {
   if constexpr (EB == 2) {
     if constexpr (RB % 256 == 0) return (k & 3) << 2;
     else return ((k >> 1) & 1) << 2;
   } else {
-    if constexpr (RB % 128 == 0) return k & 7;
+    if constexpr (RB % 256 == 0) return (k & 7) << 1;
+    else if constexpr (RB % 128 == 0) return k & 7;
     else return (k >> 1) & 3;
   }
 }
