@@ -29,9 +29,11 @@ __device__ __forceinline__ uint32_t valid_bits(int w, int V) {
 // not a candidate).
 __device__ __forceinline__ int class_pos(const uint32_t* __restrict__ bits,
                                          const int32_t* __restrict__ wpre, int c) {
+  // both words are loaded before either is used (no load waits alone behind a branch)
   const uint32_t m = bits[c >> 5];
+  const int pre = wpre[c >> 5];
   const int b = c & 31;
-  return ((m >> b) & 1u) ? wpre[c >> 5] + __popc(m & ((1u << b) - 1u)) : -1;
+  return ((m >> b) & 1u) ? pre + __popc(m & ((1u << b) - 1u)) : -1;
 }
 
 // Dynamic LDS: 2 * ceil(V/32) words when mark_lds (V <= SCE_MAX_V_SAMPLED), else none.
@@ -248,18 +250,21 @@ __global__ __launch_bounds__(256) void k_remap_gather(
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   int n = 0;
   if (t < T) {
+    // Both labels, then (sampled) their bitmap words, each set of loads issued before
+    // any of them is used; a label outside [0, V) looks up class 0 and is dropped.
     const int64_t y = targets[t];
-    int tp = -1;
-    if (y >= 0 && y < V) tp = P == 0 ? (int)y : class_pos(bits, wpre, (int)y);
-    target_pos[t] = tp;
-    n += tp >= 0;
-    int pp = -1;
-    if (prefix != nullptr) {
-      const int64_t p = prefix[t];
-      if (p >= 0 && p < V) pp = P == 0 ? (int)p : class_pos(bits, wpre, (int)p);
+    const int64_t p = prefix != nullptr ? prefix[t] : -1;
+    const bool yv = y >= 0 && y < V, pv = p >= 0 && p < V;
+    int tp = yv ? (int)y : -1, pp = pv ? (int)p : -1;
+    if (P > 0) {
+      const int tq = class_pos(bits, wpre, yv ? (int)y : 0);
+      const int pq = prefix != nullptr ? class_pos(bits, wpre, pv ? (int)p : 0) : -1;
+      tp = yv ? tq : -1;
+      pp = pv ? pq : -1;
     }
+    target_pos[t] = tp;
     prefix_pos[t] = pp;
-    n += pp >= 0;
+    n += (tp >= 0) + (pp >= 0);
   }
   const int s = block_sum_int(n, scratch);
   if (threadIdx.x == 0 && s) atomicAdd(&counters[kNumLabels], s);

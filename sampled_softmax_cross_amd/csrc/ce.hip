@@ -148,17 +148,17 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
   constexpr int E = RV::kElems;
   static_assert(!G8 || E == 8, "e4m3 output from bf16 rows");
   __shared__ float red[2 * (NT / kWave)];
-  __shared__ float zlab[2];
   const int t = blockIdx.x;
   TZ* row = Z + (int64_t)t * ldz;
   uint4* rowv = reinterpret_cast<uint4*>(row);
   const int nvec = (int)(ldz / E);  // vectors in the padded row
   const int tp = tpos[t];
   const int pp = ppos[t];
-  if (threadIdx.x == 0) {
-    zlab[0] = tp >= 0 ? RV::load1(row + tp) : 0.f;
-    zlab[1] = pp >= 0 ? RV::load1(row + pp) : 0.f;
-  }
+  // The labels' logits, loaded by every lane from a clamped column: no branch, so no
+  // wait before the row's own loads go out. The barrier of the row merge completes
+  // them before any lane writes the gradient over the row.
+  const float zt = RV::load1(row + (tp >= 0 ? tp : 0));
+  const float zp = RV::load1(row + (pp >= 0 ? pp : 0));
 
   // The row stays in registers as loaded. Short rows (up to 40 values per lane) keep
   // exp(Z - m_lane) per element after the first sweep, so the gradient costs one
@@ -200,10 +200,13 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
         s += v[k][e];
       }
   } else {
+    // Every load is issued before the first use: a lane past the row's last vector
+    // reads that vector again (the sweeps below skip it). A load under a branch
+    // would be followed, inside the branch, by a wait for that one load.
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int i = threadIdx.x + k * NT;
-      q[k] = i < nvec ? ld_stream(rowv + i) : make_uint4(0, 0, 0, 0);
+      q[k] = ld_stream(rowv + (i < nvec ? i : nvec - 1));
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -280,8 +283,8 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
   }
   if (threadIdx.x == 0) {
     float l = 0.f;
-    if (tp >= 0) l += L - zlab[0];
-    if (pp >= 0) l += L - zlab[1];
+    if (tp >= 0) l += L - zt;
+    if (pp >= 0) l += L - zp;
     row_loss[t] = l;
     if (row_lse) row_lse[t] = L;
   }
@@ -394,17 +397,15 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
   constexpr int E = RV::kElems;
   static_assert(!G8 || E == 8, "e4m3 output from bf16 rows");
   __shared__ float red[2 * (NT / kWave)];
-  __shared__ float zlab[2];
   const int t = blockIdx.x;
   TZ* row = Z + (int64_t)t * ldz;
   uint4* rowv = reinterpret_cast<uint4*>(row);
   const int nvec = (int)(ldz / E);
   const int tp = tpos[t];
   const int pp = ppos[t];
-  if (threadIdx.x == 0) {
-    zlab[0] = tp >= 0 ? RV::load1(row + tp) : 0.f;
-    zlab[1] = pp >= 0 ? RV::load1(row + pp) : 0.f;
-  }
+  // the labels' logits: every lane, clamped column, no branch (as in k_ce_rows)
+  const float zt = RV::load1(row + (tp >= 0 ? tp : 0));
+  const float zp = RV::load1(row + (pp >= 0 ? pp : 0));
   float m = -INFINITY, s = 0.f;
   for (int i = threadIdx.x; i < nvec; i += NT) {
     float f[E];
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
     if (t == 0 && threadIdx.x == 0) write_grad_scales(go, ginv);
   const float inv = N > 0 ? 1.0f / (float)N * ginv : 0.f;  // ginv: exact power of two
   const float c = (float)((tp >= 0) + (pp >= 0)) * inv;
-  __syncthreads();  // zlab was read before any lane writes the row
+  __syncthreads();  // every lane's label loads complete before any lane writes the row
   for (int i = threadIdx.x; i < nvec; i += NT) {
     float f[E];
     RV::unpack(ld_stream(rowv + i), f);
@@ -445,8 +446,8 @@ __global__ __launch_bounds__(NT) void k_ce_rows_stream(TZ* __restrict__ Z, int64
   }
   if (threadIdx.x == 0) {
     float l = 0.f;
-    if (tp >= 0) l += L - zlab[0];
-    if (pp >= 0) l += L - zlab[1];
+    if (tp >= 0) l += L - zt;
+    if (pp >= 0) l += L - zp;
     row_loss[t] = l;
     if (row_lse) row_lse[t] = L;
   }

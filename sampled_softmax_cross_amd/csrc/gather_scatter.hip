@@ -17,22 +17,29 @@ namespace sce {
 constexpr int kCopyThreads = 256;
 
 // loss = sum of the rows' loss terms / N, summed by one block in a fixed order.
+// Each lane issues all the loads of a round (kLossRows rows, a block apart: 8192
+// rows per round) before its first add, which it makes in row order. The loads are
+// unconditional (rows past T read row T - 1 and count as zero): a load under a
+// branch would have its conversion placed in the same branch, behind a wait for that
+// one load, which turns the round into kLossRows round trips to memory.
+constexpr int kLossRows = 32;
 __device__ void finish_loss(const LossOut& f) {
   __shared__ double part[kCopyThreads / kWave];
-  // Eight independent partial sums per lane keep eight loads in flight; lane l adds
-  // rows l + 256 (8k + j) into partial j, and the partials are added in order j.
-  constexpr int kAcc = 8;
-  double a[kAcc] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-  for (int t0 = threadIdx.x; t0 < f.T; t0 += kCopyThreads * kAcc) {
-#pragma unroll
-    for (int j = 0; j < kAcc; ++j) {
-      const int t = t0 + j * kCopyThreads;
-      if (t < f.T) a[j] += (double)f.row_loss[t];
-    }
-  }
+  // the counters travel with the first round of loads
+  const int N = f.counters[kNumLabels], distinct = f.counters[kDistinct],
+            next_off = f.counters[kNextOffset], status = f.counters[kStatus];
   double acc = 0.0;
+  for (int t0 = threadIdx.x; t0 < f.T; t0 += kCopyThreads * kLossRows) {
+    float v[kLossRows];
 #pragma unroll
-  for (int j = 0; j < kAcc; ++j) acc += a[j];
+    for (int j = 0; j < kLossRows; ++j) {
+      const int t = t0 + j * kCopyThreads;
+      const float x = f.row_loss[t < f.T ? t : f.T - 1];
+      v[j] = t < f.T ? x : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kLossRows; ++j) acc += (double)v[j];
+  }
   acc = wave_sum(acc);
   if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
   __syncthreads();
@@ -40,13 +47,12 @@ __device__ void finish_loss(const LossOut& f) {
     double tot = 0.0;
 #pragma unroll
     for (int w = 0; w < kCopyThreads / kWave; ++w) tot += part[w];
-    const int N = f.counters[kNumLabels];
     *f.loss = N > 0 ? (float)(tot / (double)N) : 0.f;
     if (f.aux) {
-      f.aux[0] = f.counters[kDistinct];
+      f.aux[0] = distinct;
       f.aux[1] = N;
-      f.aux[2] = f.counters[kNextOffset];
-      f.aux[3] = f.counters[kStatus];
+      f.aux[2] = next_off;
+      f.aux[3] = status;
     }
   }
 }
@@ -92,6 +98,17 @@ __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
   const uint32_t vpr = (uint32_t)d / 8;
   const uint32_t total = (uint32_t)rows * vpr;
   const uint32_t i0 = (uint32_t)b * kPerBlock + threadIdx.x;
+  // Destination rows first, loaded unconditionally (a vector past the end takes the
+  // last one's row and is not stored), so the class loads travel with the others
+  // rather than each waiting alone in front of its store.
+  uint32_t dst[kScatterVecs];
+#pragma unroll
+  for (int u = 0; u < kScatterVecs; ++u) {
+    const uint32_t i = i0 + u * kCopyThreads;
+    const uint32_t ic = i < total ? i : total - 1;
+    const uint32_t p = ic / vpr, c8 = ic - p * vpr;
+    dst[u] = (C ? (uint32_t)C[p] : p) * vpr + c8;
+  }
   float4 lo[kScatterVecs], hi[kScatterVecs];
 #pragma unroll
   for (int u = 0; u < kScatterVecs; ++u) {
@@ -119,13 +136,8 @@ __global__ __launch_bounds__(kCopyThreads) void k_scatter_rows(
     }
   }
 #pragma unroll
-  for (int u = 0; u < kScatterVecs; ++u) {
-    const uint32_t i = i0 + u * kCopyThreads;
-    if (i >= total) continue;
-    const uint32_t p = i / vpr, c8 = i - p * vpr;
-    const uint32_t row = C ? (uint32_t)C[p] : p;
-    store_vec<BF16>(dW, (size_t)row * vpr + c8, lo[u], hi[u]);
-  }
+  for (int u = 0; u < kScatterVecs; ++u)
+    if (i0 + u * kCopyThreads < total) store_vec<BF16>(dW, dst[u], lo[u], hi[u]);
 }
 
 // out[i, :] = W[idx[i], :] for i < n (rows of row_vecs 16-byte vectors, out rows

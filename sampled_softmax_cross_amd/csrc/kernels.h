@@ -54,7 +54,8 @@ __device__ __forceinline__ void gather_rows_block(int blk, const uint4* __restri
 }
 // Zero rows of the dense gradient: block `blk` covers kZeroVecs 16-byte vectors of the
 // flat [V, vpr] array (vpr vectors per row) and clears those of rows outside C (bit
-// clear in the candidate bitmap): one lookup per vector, then stores only.
+// clear in the candidate bitmap): one lookup per vector, all four of a lane issued
+// before the first is tested (a vector past the end looks up row 0), then stores only.
 constexpr int kZeroVecs = 256 * 4;
 inline int zero_block_count(int V, int vpr) {
   return (int)(((int64_t)V * vpr + kZeroVecs - 1) / kZeroVecs);
@@ -63,13 +64,17 @@ __device__ __forceinline__ void zero_rows_block(int blk, const uint32_t* __restr
                                                 int vpr, uint4* __restrict__ dW) {
   const int64_t total = (int64_t)V * vpr;
   const int64_t i0 = (int64_t)blk * kZeroVecs + threadIdx.x;
-  bool in_c[4];
+  uint32_t word[4];
+  int row[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t i = i0 + u * 256;
-    const int row = i < total ? (int)(i / vpr) : 0;
-    in_c[u] = i >= total || ((bits[row >> 5] >> (row & 31)) & 1u);
+    row[u] = i < total ? (int)(i / vpr) : 0;
+    word[u] = bits[row[u] >> 5];
   }
+  bool in_c[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) in_c[u] = i0 + u * 256 >= total || ((word[u] >> (row[u] & 31)) & 1u);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     if (!in_c[u]) dW[i0 + u * 256] = make_uint4(0, 0, 0, 0);
