@@ -264,8 +264,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
   // first fragments go to buffer 0.
   static_assert(KS >= 2 && KS % 2 == 0 && NSB >= 2 && NSB <= NS && WAIT0 < 64, "pipeline shape");
   // Equal depths: stage s holds its A tile then its B tile (one slot of A_SLOT + B_SLOT);
-  // otherwise an A ring followed by a B ring.
-  __shared__ uint4 lds[NS * A_SLOT + NSB * B_SLOT];
+  // otherwise an A ring followed by a B ring. A bf16 output whose wave slices are 64
+  // columns wide goes out through 4 KB of LDS per wave past the ring, when that fits
+  // beside it (one workgroup per CU, 160 KB): see store_acc_bf16_lds.
+  constexpr int kRing = NS * A_SLOT + NSB * B_SLOT;
+  constexpr bool kStaged = OUT == kOutBF16 && TN == 2 && OCC == 1 && (kRing + NW * 256) * 16 <= 160 * 1024;
+  __shared__ uint4 lds[kRing + (kStaged ? NW * 256 : 0)];
   auto a_slot = [&](int i) { return lds + (NSB == NS ? i * (A_SLOT + B_SLOT) : i * A_SLOT); };
   auto b_slot = [&](int i) {
     return lds + (NSB == NS ? i * (A_SLOT + B_SLOT) + A_SLOT : NS * A_SLOT + i * B_SLOT);
@@ -446,8 +450,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc;
     }
-    store_acc<OUT, TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow + l32, cc.n0 + bcol, lane >> 5,
-                           OUT == kOutF32Split ? (cc.kb / kps) * split_stride : 0);
+    if constexpr (kStaged)
+      store_acc_bf16_lds<TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow, cc.n0 + bcol, lane,
+                                 lds + kRing + wid * 256);
+    else
+      store_acc<OUT, TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow + l32, cc.n0 + bcol, lane >> 5,
+                             OUT == kOutF32Split ? (cc.kb / kps) * split_stride : 0);
   }
   // The ring's last loads (of stages past the last unit: zeros) land before the
   // workgroup's LDS is released.

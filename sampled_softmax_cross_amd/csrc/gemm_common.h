@@ -183,4 +183,55 @@ __device__ __forceinline__ void store_acc(f32x16_t (&acc)[TM][TN], void* __restr
   }
 }
 
+// bf16 output of a wave whose slice is 64 columns wide (TN = 2), restaged through
+// `stage` (4 KB of LDS owned by the wave) one 32-row block at a time: each lane writes
+// its row's four 16-byte pieces (column chunks c = 4j + 2gp + half, placed at chunk
+// slot c ^ (row & 7) so that eight lanes of one chunk hit all 32 banks), then reads
+// back eight rows of eight chunks per instruction, so that every store instruction
+// writes eight whole 128-byte rows instead of 32-byte pieces of 32 rows (the same 16
+// stores per lane; the logits product spends less time in its epilogue).
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc_bf16_lds(f32x16_t (&acc)[TM][TN], void* __restrict__ Cout,
+                                                   int64_t ldc, int64_t M, int64_t N, int64_t row0,
+                                                   int64_t col0, int lane, uint4* __restrict__ stage) {
+  static_assert(TN == 2, "64-column wave slices: eight 16-byte chunks per row");
+  bf16_t* out = static_cast<bf16_t*>(Cout);
+  const int64_t ncols = (N + 7) / 8 * 8;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int rr = lane >> 3, cc = lane & 7;  // read-back: row rr of each group of 8, chunk cc
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const int g0 = 4 * (2 * gp), g1 = 4 * (2 * gp + 1);
+        uint32_t e0 = pack_bf16x2(acc[i][j][g0 + 0], acc[i][j][g0 + 1]);
+        uint32_t e1 = pack_bf16x2(acc[i][j][g0 + 2], acc[i][j][g0 + 3]);
+        uint32_t o0 = pack_bf16x2(acc[i][j][g1 + 0], acc[i][j][g1 + 1]);
+        uint32_t o1 = pack_bf16x2(acc[i][j][g1 + 2], acc[i][j][g1 + 3]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(e0, o0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(e1, o1, false, false);
+        const int c = 4 * j + 2 * gp + half;
+        stage[l32 * 8 + (c ^ (l32 & 7))] = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      }
+    }
+    // the wave's LDS writes complete before any lane reads another lane's row
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * q + rr;
+      v[q] = stage[r * 8 + (cc ^ (r & 7))];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next block's writes
+    const int64_t col = col0 + 8 * cc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = row0 + i * 32 + 8 * q + rr;
+      if (row < M && col < ncols) *reinterpret_cast<uint4*>(out + row * ldc + col) = v[q];
+    }
+  }
+}
+
 }  // namespace sce
