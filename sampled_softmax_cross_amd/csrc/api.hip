@@ -334,11 +334,14 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
 
   StageMarks marks(hs);
   marks.mark(SCE_STAGE_CANDIDATES);
+  int amax_parts = 0;  // max|x| partials, taken beside the candidate build
   hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
                                    (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
                                    tpos, ppos,
-                                   W8, (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2), hs);
-  if (e == hipSuccess) e = launch_quant_x(x, T * d, counters, w_scale, x8, scales, scales_out, hs);
+                                   W8, (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2), hs,
+                                   x, T * d, &amax_parts);
+  if (e == hipSuccess)
+    e = launch_quant_x(x, T * d, counters, w_scale, x8, scales, scales_out, hs, amax_parts);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
     GemmArgs g{x8, d, WC, p.ldwc, Z, p.ldz, T, p.Peff, d, 1, 0, scales + kScaleLogits};

@@ -47,7 +47,15 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
                                                         bool mark_lds, int32_t* __restrict__ C,
                                                         uint32_t* __restrict__ bits,
                                                         int32_t* __restrict__ wpre,
-                                                        int32_t* __restrict__ counters) {
+                                                        int32_t* __restrict__ counters,
+                                                        const uint4* __restrict__ amax_x,
+                                                        int64_t amax_nvec) {
+  // Blocks past the first: the e4m3 step's max|x| (one partial each), which needs
+  // nothing from the build and runs beside it on the otherwise idle chip.
+  if (blockIdx.x > 0) {
+    amax_bf16_block(amax_x, amax_nvec, (int)blockIdx.x - 1, (int)gridDim.x - 1, counters);
+    return;
+  }
   extern __shared__ uint32_t lds_words[];
   __shared__ int scratch[kBuildThreads / kWave + 1];
   const int W = (V + 31) >> 5;
@@ -91,8 +99,11 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
   int cnt = 0;
   if (mark_lds)
     for (int w = tid; w < W; w += nt) cnt += __popc(mark[w]);
-  const int distinct = block_sum_int(cnt, scratch);   // (contains barriers)
-  const int any_bad = block_sum_int(bad, scratch);
+  // One block sum carries both: the distinct count (below 2^20: V <= 131072 when the
+  // bitmap is in LDS, else 0) and, above it, the lanes that met a bad label (<= 1024).
+  const int packed = block_sum_int(cnt + (bad << 20), scratch);  // (contains barriers)
+  const int distinct = packed & ((1 << 20) - 1);
+  const int any_bad = packed >> 20;
   if (P == 0) {
     if (tid == 0) {
       counters[kStatus] = any_bad ? kDevLabelRange : 0;
@@ -284,11 +295,15 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                              int stride, int off, int32_t* counters, int32_t* C, uint32_t* bits,
                              int32_t* wpre, int32_t* vocab_pos, int32_t* target_pos,
                              int32_t* prefix_pos, const void* W, int row_bytes, void* WC,
-                             int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s) {
+                             int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s,
+                             const void* amax_x, int64_t amax_n, int* amax_parts) {
   const bool mark_lds = V <= kMaxBitmapClasses;
   const size_t lds = mark_lds ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
-  hipLaunchKernelGGL(k_cand, dim3(1), dim3(kBuildThreads), lds, s, targets, prefix, T, V, P,
-                     stride, off, mark_lds, C, bits, wpre, counters);
+  const int agrid = amax_n >= 0 ? amax_block_count(amax_n / 8) : 0;
+  if (amax_parts) *amax_parts = agrid;
+  hipLaunchKernelGGL(k_cand, dim3(1 + agrid), dim3(kBuildThreads), lds, s, targets, prefix, T, V,
+                     P, stride, off, mark_lds, C, bits, wpre, counters,
+                     static_cast<const uint4*>(amax_x), amax_n / 8);
   const int remap_blocks = (T + 255) / 256;
   const int gather_blocks = (W != nullptr && P > 0) ? gather_block_count(P, row_bytes / 16) : 0;
   const int zero_blocks = (dW != nullptr && P > 0) ? zero_block_count(V, dw_row_bytes / 16) : 0;

@@ -15,11 +15,16 @@ constexpr int kMaxBitmapClasses = 131072;
 // and, when P > 0: with W, the row gather W_C = W[C] (rows of row_bytes, a multiple of
 // 16); with dW, the rows of the dense gradient outside C set to zero (rows of
 // dw_row_bytes, a multiple of 16); with vocab_pos, the class -> position map.
+// With amax_n >= 0 the build's launch also takes max|x| over amax_x (bf16, amax_n
+// elements, a multiple of 8; null when amax_n == 0) in *amax_parts partials
+// (counters[kAmaxX + i]) for launch_quant_x.
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
                              int stride, int off, int32_t* counters, int32_t* C, uint32_t* bits,
                              int32_t* wpre, int32_t* vocab_pos, int32_t* target_pos,
                              int32_t* prefix_pos, const void* W, int row_bytes, void* WC,
-                             int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s);
+                             int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s,
+                             const void* amax_x = nullptr, int64_t amax_n = -1,
+                             int* amax_parts = nullptr);
 hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s);
 
 // Row gather, one block of 256 lanes per kGatherRows rows: 32 lanes per row, each
@@ -127,11 +132,62 @@ hipError_t launch_ce_rows_g8(const void* Z, int64_t ldz, int T, int P, const int
                              const int32_t* prefix_pos, const int32_t* counters, float* row_loss,
                              float* row_lse, const G8Out& go, hipStream_t s);
 
-// e4m3 step: max|x| over bf16 x [n] (n a multiple of 8), s_x, and x8 = e4m3(x / s_x)
+// e4m3 step: s_x from max|x| over bf16 x [n] (n a multiple of 8), and x8 = e4m3(x / s_x)
 // (bytes, same layout); fills the scale table's x entries (w_scale, s_x) and
-// scales_out[0] when given. counters[kAmaxX] must be zero on entry.
+// scales_out[0] when given. max|x| comes from the amax_parts partials that
+// launch_candidates left in counters[kAmaxX ...] (amax_parts > 0), else from an amax
+// launch of its own.
 hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_scale, void* x8,
-                          float* scales, float* scales_out, hipStream_t s);
+                          float* scales, float* scales_out, hipStream_t s, int amax_parts = 0);
+
+// max|x| partial of one amax block (kBuildThreads lanes; block `b` of `nb`) over nvec
+// 16-byte bf16 vectors, written as the magnitude's bits to counters[kAmaxX + b].
+constexpr int kAmaxLoads = 8;
+inline int amax_block_count(int64_t nvec) {
+  const int64_t want = (nvec + (int64_t)kBuildThreads * kAmaxLoads - 1) / ((int64_t)kBuildThreads * kAmaxLoads);
+  return (int)(want < 1 ? 1 : (want > kAmaxSlots ? kAmaxSlots : want));
+}
+// Magnitude bits of the largest |x| of 8 bf16 values (bf16 magnitudes order like their
+// bit patterns).
+__device__ __forceinline__ uint32_t amax8(const uint4& q) {
+  uint32_t m = 0;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, w[i] & 0x7fffu);
+    m = max(m, (w[i] >> 16) & 0x7fffu);
+  }
+  return m;
+}
+// Each block writes the largest magnitude it saw to its own partial (no atomics:
+// atomics on one address serialise, one per workgroup of 512 measured 10.8 us for a
+// 25 MB tensor); kAmaxLoads loads in flight per lane, all issued before the first use.
+__device__ __forceinline__ void amax_bf16_block(const uint4* __restrict__ x, int64_t nvec, int b,
+                                                int nb, int32_t* __restrict__ counters) {
+  __shared__ uint32_t wmax[kBuildThreads / 64];
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)nb * kBuildThreads;
+  for (int64_t i0 = (int64_t)b * kBuildThreads + threadIdx.x; i0 < nvec; i0 += kAmaxLoads * stride) {
+    uint4 q[kAmaxLoads];
+#pragma unroll
+    for (int j = 0; j < kAmaxLoads; ++j) {
+      const int64_t i = i0 + j * stride;
+      q[j] = x[i < nvec ? i : nvec - 1];  // past the end: the last vector again (no change)
+    }
+#pragma unroll
+    for (int j = 0; j < kAmaxLoads; ++j) m = max(m, amax8(q[j]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kBuildThreads / 64; ++w) t = max(t, wmax[w]);
+    counters[kAmaxX + b] = (int32_t)t;
+  }
+}
 
 
 // GEMMs. Matrices row-major; see gemm.hip for the operand conventions.

@@ -6,53 +6,15 @@
 // so x / s_x is exact and the conversion (round to nearest even, OCP E4M3, the
 // hardware's v_cvt_pk_fp8_f32) is the only rounding.
 //
-// Two launches: the amax of |x| over the whole tensor (per-workgroup maxima of the
-// bf16 magnitude bits, which order like the values), then the conversion, whose
-// workgroups each reduce those maxima, derive s_x from the amax in integers and write
-// the step's scale table.
+// The amax of |x| over the whole tensor (per-workgroup maxima of the bf16 magnitude
+// bits, which order like the values) is taken by extra workgroups of the candidate
+// build's launch (amax_bf16_block), which runs on one workgroup and leaves the rest of
+// the chip idle; the conversion's workgroups each reduce those maxima, derive s_x from
+// the amax in integers and write the step's scale table.
 #include "common.h"
 #include "kernels.h"
 
 namespace sce {
-
-// Magnitude bits of the largest |x| of 8 bf16 values.
-__device__ __forceinline__ uint32_t amax8(const uint4& q) {
-  uint32_t m = 0;
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = max(m, w[i] & 0x7fffu);
-    m = max(m, (w[i] >> 16) & 0x7fffu);
-  }
-  return m;
-}
-
-// Each workgroup writes the largest magnitude it saw to its own partial (no atomics:
-// atomics on one address serialise, one per workgroup of 512 measured 10.8 us for a
-// 25 MB tensor); eight loads in flight per lane.
-__global__ __launch_bounds__(256) void k_amax_bf16(const uint4* __restrict__ x, int64_t nvec,
-                                                   int32_t* __restrict__ counters) {
-  __shared__ uint32_t wmax[256 / kWave];
-  constexpr int kLoads = 8;
-  uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < nvec; i0 += kLoads * stride) {
-    uint4 q[kLoads];
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int64_t i = i0 + j * stride;
-      q[j] = i < nvec ? x[i] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) m = max(m, amax8(q[j]));
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
-  if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    counters[kAmaxX + blockIdx.x] = (int32_t)max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-}
 
 // s_x = 2^e from the bf16 magnitude bits of max|x|: with max|x| = f 2^E, f in [0.5, 1),
 // 448 2^e = 0.875 2^(e + 9) covers it first at e = E - 9 when f <= 0.875, else at
@@ -118,15 +80,13 @@ __global__ __launch_bounds__(256) void k_quant_e4m3(const uint4* __restrict__ x,
 }
 
 hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_scale, void* x8,
-                          float* scales, float* scales_out, hipStream_t s) {
+                          float* scales, float* scales_out, hipStream_t s, int amax_parts) {
+  if (amax_parts < 1 || amax_parts > kAmaxSlots) return hipErrorInvalidValue;
   const int64_t nvec = n / 8;
   const int64_t want = (nvec + 255) / 256;
   const int grid = (int)(want < 2048 ? (want > 0 ? want : 1) : 2048);
-  const int agrid = grid < kAmaxSlots ? grid : kAmaxSlots;
-  hipLaunchKernelGGL(k_amax_bf16, dim3(agrid), dim3(256), 0, s, static_cast<const uint4*>(x), nvec,
-                     counters);
   hipLaunchKernelGGL(k_quant_e4m3, dim3(grid), dim3(256), 0, s, static_cast<const uint4*>(x), nvec,
-                     counters, agrid, w_scale, static_cast<uint2*>(x8), scales, scales_out);
+                     counters, amax_parts, w_scale, static_cast<uint2*>(x8), scales, scales_out);
   return hipGetLastError();
 }
 
