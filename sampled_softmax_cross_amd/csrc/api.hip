@@ -248,8 +248,10 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
                                    (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
                                    tpos, ppos,
                                    W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), dW,
-                                   (int)(d * es), hs);
-  if (e == hipSuccess && bf16 && T > 0)
+                                   (int)(d * es), hs, nullptr, -1, nullptr,
+                                   bf16 && T > 0 ? ws + p.wt : nullptr, p.ldt);
+  // bf16: dX reads W_C transposed; the gather wrote it when P > 0, W's own is made here
+  if (e == hipSuccess && bf16 && T > 0 && P == 0)
     e = launch_transpose(WC, p.ldwc, (int)p.Peff, (int)d, 2, ws + p.wt, p.ldt, hs);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {

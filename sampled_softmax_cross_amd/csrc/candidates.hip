@@ -231,7 +231,8 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
 }
 
 // Blocks [0, remap_blocks): labels -> positions in C (identity when P == 0), count N.
-// The next gather_blocks: the row gather W_C = W[C] (none when P == 0). The next
+// The next gather_blocks: the row gather W_C = W[C] (none when P == 0), or with WT
+// (bf16) tiles that gather and transpose: W_C and WT = W_C^T from one read. The next
 // zero_blocks: the rows of the dense gradient outside C set to zero (written here,
 // while the memory system is otherwise idle, rather than beside the candidate rows at
 // the end of the step). The rest: vocab_pos[c] = position of c in C, or -1.
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void k_remap_gather(
     int32_t* __restrict__ counters, int remap_blocks, const uint4* __restrict__ W,
     const int32_t* __restrict__ C, int row_vecs, uint4* __restrict__ WC, int wc_vecs,
     int gather_blocks, uint4* __restrict__ dW, int dw_vecs, int zero_blocks,
-    int32_t* __restrict__ vocab_pos) {
+    int32_t* __restrict__ vocab_pos, uint16_t* __restrict__ WT, int64_t ldt, int tr_x) {
   const int b = (int)blockIdx.x;
   if (b >= remap_blocks + gather_blocks + zero_blocks) {
     const int c = (b - remap_blocks - gather_blocks - zero_blocks) * 256 + (int)threadIdx.x;
@@ -254,7 +255,13 @@ __global__ __launch_bounds__(256) void k_remap_gather(
     return;
   }
   if ((int)blockIdx.x >= remap_blocks) {
-    gather_rows_block((int)blockIdx.x - remap_blocks, W, C, P, row_vecs, WC, wc_vecs);
+    const int g = (int)blockIdx.x - remap_blocks;
+    if (WT)
+      transpose_tile<uint16_t>(g % tr_x, g / tr_x, reinterpret_cast<const uint16_t*>(W),
+                               (int64_t)row_vecs * 8, C, P, row_vecs * 8, WT, ldt,
+                               reinterpret_cast<uint16_t*>(WC), (int64_t)wc_vecs * 8);
+    else
+      gather_rows_block(g, W, C, P, row_vecs, WC, wc_vecs);
     return;
   }
   __shared__ int scratch[256 / kWave + 1];
@@ -296,7 +303,8 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                              int32_t* wpre, int32_t* vocab_pos, int32_t* target_pos,
                              int32_t* prefix_pos, const void* W, int row_bytes, void* WC,
                              int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s,
-                             const void* amax_x, int64_t amax_n, int* amax_parts) {
+                             const void* amax_x, int64_t amax_n, int* amax_parts, void* WT,
+                             int64_t ldt) {
   const bool mark_lds = V <= kMaxBitmapClasses;
   const size_t lds = mark_lds ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
   const int agrid = amax_n >= 0 ? amax_block_count(amax_n / 8) : 0;
@@ -305,7 +313,12 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                      P, stride, off, mark_lds, C, bits, wpre, counters,
                      static_cast<const uint4*>(amax_x), amax_n / 8);
   const int remap_blocks = (T + 255) / 256;
-  const int gather_blocks = (W != nullptr && P > 0) ? gather_block_count(P, row_bytes / 16) : 0;
+  // with WT: gather-and-transpose tiles, kTrTile rows of W_C by kTrTile of its columns
+  const bool tr = WT != nullptr && W != nullptr && P > 0;
+  const int tr_x = tr ? (int)((ldt + kTrTile - 1) / kTrTile) : 1;
+  const int gather_blocks =
+      tr ? tr_x * ((row_bytes / 2 + kTrTile - 1) / kTrTile)
+         : ((W != nullptr && P > 0) ? gather_block_count(P, row_bytes / 16) : 0);
   const int zero_blocks = (dW != nullptr && P > 0) ? zero_block_count(V, dw_row_bytes / 16) : 0;
   const int map_blocks = (vocab_pos != nullptr && P > 0) ? (V + 255) / 256 : 0;
   const int grid = remap_blocks + gather_blocks + zero_blocks + map_blocks;
@@ -314,7 +327,8 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                        wpre, target_pos, prefix_pos, counters, remap_blocks,
                        reinterpret_cast<const uint4*>(W), C, row_bytes / 16,
                        reinterpret_cast<uint4*>(WC), wc_row_bytes / 16, gather_blocks,
-                       reinterpret_cast<uint4*>(dW), dw_row_bytes / 16, zero_blocks, vocab_pos);
+                       reinterpret_cast<uint4*>(dW), dw_row_bytes / 16, zero_blocks, vocab_pos,
+                       static_cast<uint16_t*>(tr ? WT : nullptr), ldt, tr_x);
   return hipGetLastError();
 }
 

@@ -183,44 +183,18 @@ hipError_t launch_gather_checked(const void* W, int64_t V, const int32_t* idx, i
   return hipGetLastError();
 }
 
-// Tiled transpose through LDS: a block moves a 64 x 64-element tile; it reads 16-byte
-// chunks along the source rows and writes 16-byte chunks along the destination rows, so
-// both sides stay coalesced. The LDS rows are padded by one 4-byte word so the
-// column-wise reads of a chunk fall on different banks.
-constexpr int kTile = 64;
+// Tiled transpose through LDS (transpose_tile in kernels.h), one tile per block.
 template <typename E>
 __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ src, int64_t ld_src,
                                                    int rows, int cols, E* __restrict__ dst,
                                                    int64_t ld_dst) {
-  constexpr int EPC = 16 / sizeof(E);        // elements per 16-byte chunk
-  constexpr int CPR = kTile / EPC;           // chunks per tile row
-  constexpr int LDT = kTile + 4 / sizeof(E); // padded LDS row (elements)
-  __shared__ E tile[kTile * LDT];
-  const int r0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
-  for (int q = threadIdx.x; q < kTile * CPR; q += 256) {
-    const int r = q / CPR, c = (q % CPR) * EPC;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < rows && c0 + c < cols)
-      v = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * ld_src + c0 + c);
-    const E* e = reinterpret_cast<const E*>(&v);
-#pragma unroll
-    for (int i = 0; i < EPC; ++i) tile[r * LDT + c + i] = e[i];
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < kTile * CPR; q += 256) {
-    const int c = q / CPR, r = (q % CPR) * EPC;  // destination row c, columns r .. r + EPC
-    if (c0 + c >= cols || r0 + r >= ld_dst) continue;
-    uint4 v;
-    E* e = reinterpret_cast<E*>(&v);
-#pragma unroll
-    for (int i = 0; i < EPC; ++i) e[i] = tile[(r + i) * LDT + c];
-    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * ld_dst + r0 + r) = v;
-  }
+  transpose_tile<E>((int)blockIdx.x, (int)blockIdx.y, src, ld_src, nullptr, rows, cols, dst, ld_dst,
+                    nullptr, 0);
 }
 
 hipError_t launch_transpose(const void* src, int64_t ld_src, int rows, int cols, int es, void* dst,
                             int64_t ld_dst, hipStream_t s) {
-  const dim3 grid((unsigned)((ld_dst + kTile - 1) / kTile), (unsigned)((cols + kTile - 1) / kTile));
+  const dim3 grid((unsigned)((ld_dst + kTrTile - 1) / kTrTile), (unsigned)((cols + kTrTile - 1) / kTrTile));
   if (grid.x == 0 || grid.y == 0) return hipGetLastError();
   if (es == 2)
     hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src),

@@ -13,9 +13,10 @@ constexpr int kMaxBitmapClasses = 131072;
 // Candidate build (P > 0: C, and the candidate bitmap `bits` and per-word prefix
 // counts `wpre`, ceil(V/32) words each) or label check (P == 0), then the label remap
 // and, when P > 0: with W, the row gather W_C = W[C] (rows of row_bytes, a multiple of
-// 16); with dW, the rows of the dense gradient outside C set to zero (rows of
-// dw_row_bytes, a multiple of 16); with vocab_pos, the class -> position map.
-// With amax_n >= 0 the build's launch also takes max|x| over amax_x (bf16, amax_n
+// 16; with WT, bf16 rows only, the gather writes W_C and its transpose WT [d, ldt],
+// zeros past P, in one pass); with dW, the rows of the dense gradient outside C set to
+// zero (rows of dw_row_bytes, a multiple of 16); with vocab_pos, the class -> position
+// map. With amax_n >= 0 the build's launch also takes max|x| over amax_x (bf16, amax_n
 // elements, a multiple of 8; null when amax_n == 0) in *amax_parts partials
 // (counters[kAmaxX + i]) for launch_quant_x.
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
@@ -24,7 +25,7 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                              int32_t* prefix_pos, const void* W, int row_bytes, void* WC,
                              int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s,
                              const void* amax_x = nullptr, int64_t amax_n = -1,
-                             int* amax_parts = nullptr);
+                             int* amax_parts = nullptr, void* WT = nullptr, int64_t ldt = 0);
 hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s);
 
 // Row gather, one block of 256 lanes per kGatherRows rows: 32 lanes per row, each
@@ -57,6 +58,49 @@ __device__ __forceinline__ void gather_rows_block(int blk, const uint4* __restri
     if (k3) dst[v0 + 96] = b3;
   }
 }
+// Tiled transpose through LDS: one block of 256 lanes moves the kTrTile x kTrTile tile
+// (bx, by) of dst[c, r] = src[map ? map[r] : r, c] (r < rows, c < cols; dst columns r in
+// [rows, ld_dst) get zeros). It reads 16-byte chunks along the source rows and writes
+// 16-byte chunks along the destination rows, so both sides stay coalesced; the LDS rows
+// are padded by one 4-byte word so the column-wise reads of a chunk fall on different
+// banks. With `copy`, the rows it read also go to copy[r, c] (the gathered rows, for a
+// gather that also transposes: its source is read once for both).
+constexpr int kTrTile = 64;
+template <typename E>
+__device__ __forceinline__ void transpose_tile(int bx, int by, const E* __restrict__ src,
+                                               int64_t ld_src, const int32_t* __restrict__ map,
+                                               int rows, int cols, E* __restrict__ dst,
+                                               int64_t ld_dst, E* __restrict__ copy,
+                                               int64_t ld_copy) {
+  constexpr int EPC = 16 / sizeof(E);           // elements per 16-byte chunk
+  constexpr int CPR = kTrTile / EPC;            // chunks per tile row
+  constexpr int LDT = kTrTile + 4 / sizeof(E);  // padded LDS row (elements)
+  __shared__ E tile[kTrTile * LDT];
+  const int r0 = bx * kTrTile, c0 = by * kTrTile;
+  for (int q = threadIdx.x; q < kTrTile * CPR; q += 256) {
+    const int r = q / CPR, c = (q % CPR) * EPC;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < rows && c0 + c < cols) {
+      const int64_t sr = map ? (int64_t)map[r0 + r] : (int64_t)(r0 + r);
+      v = *reinterpret_cast<const uint4*>(src + sr * ld_src + c0 + c);
+      if (copy) *reinterpret_cast<uint4*>(copy + (int64_t)(r0 + r) * ld_copy + c0 + c) = v;
+    }
+    const E* e = reinterpret_cast<const E*>(&v);
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) tile[r * LDT + c + i] = e[i];
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < kTrTile * CPR; q += 256) {
+    const int c = q / CPR, r = (q % CPR) * EPC;  // destination row c, columns r .. r + EPC
+    if (c0 + c >= cols || r0 + r >= ld_dst) continue;
+    uint4 v;
+    E* e = reinterpret_cast<E*>(&v);
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) e[i] = tile[(r + i) * LDT + c];
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * ld_dst + r0 + r) = v;
+  }
+}
+
 // Zero rows of the dense gradient: block `blk` covers kZeroVecs 16-byte vectors of the
 // flat [V, vpr] array (vpr vectors per row) and clears those of rows outside C (bit
 // clear in the candidate bitmap): one lookup per vector, all four of a lane issued
