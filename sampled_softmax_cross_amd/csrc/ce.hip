@@ -20,6 +20,8 @@
 namespace sce {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Rows whose lanes hold at most this many values keep exp(Z - m_lane) per element.
+constexpr int kKeepValues = 40;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename TZ>
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(NT) void k_ce_rows(TZ* __restrict__ Z, int64_t ldz,
   // keep only the packed 16-byte vectors (half the registers for bf16, so more rows
   // per CU keep loads in flight) and evaluate the exponential a second time.
   // Only the last vector of a row can hold padding columns (j >= P).
-  constexpr bool kKeep = VPT * E <= 40;
+  constexpr bool kKeep = VPT * E <= kKeepValues;
   uint4 q[kKeep ? 1 : VPT];
   float v[kKeep ? VPT : 1][E];
   float m = -INFINITY;
@@ -495,9 +497,12 @@ static void launch_ce_typed(TZ* Z, int64_t ldz, int T, int P, const int32_t* tp,
       hipLaunchKernelGGL((k_ce_rows_wave<TZ, 3, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
     else
       hipLaunchKernelGGL((k_ce_rows_wave<TZ, 4, G8>), grid, block, 0, s, Z, ldz, P, T, tp, pp, counters, rl, lse, go);
-  } else if (nvec <= 256 * 8) {
-    // up to 8 vectors per lane on 256 lanes; longer rows take 512 lanes (P = 24576 bf16:
-    // 6 vectors per lane at 70 registers ran 16% faster than 12 at 99)
+  } else if (nvec <= 256 * kKeepValues / E) {
+    // 256 lanes while they hold at most kKeepValues values each (exp(Z - m_lane) kept,
+    // not evaluated twice), then 512 lanes, kept while that fits (P = 14336 bf16: 512 x 4
+    // kept ran the CE 7.5% faster than 256 x 7 evaluated twice) and with more vectors
+    // per lane past it (P = 24576 bf16: 512 x 6 at 70 registers ran 16% faster than
+    // 256 x 12 at 99, and 1024 x 3 kept 45% slower).
     launch_ce_nt<TZ, 256, G8>((int)((nvec + 255) / 256), Z, ldz, T, P, tp, pp, counters, rl, lse,
                               go, s);
   } else if (nvec <= 512 * 16) {
