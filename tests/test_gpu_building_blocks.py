@@ -17,6 +17,12 @@ CE_CASES = [
     (300, 333, 400, "f32", True, 0.0),
     (129, 2048, 2048, "bf16", False, 0.2),
     (64, 8, 8, "f32", True, 0.0),
+    # either side of the row-shape choice: 256 lanes while 40 values each, then 512
+    # lanes with the values kept, then 512 lanes evaluating the exponential twice
+    (40, 10248, 10248, "bf16", True, 0.0),      # 1281 vectors: 512 lanes, kept
+    (24, 20488, 20488, "bf16", False, 0.1),     # 2561 vectors: 512 lanes, evaluated twice
+    (32, 9000, 9000, "f32", True, 0.0),         # 2250 vectors: 256 lanes x 9, kept
+    (24, 20488, 20488, "f32", False, 0.0),      # 5122 vectors: 512 lanes x 11, evaluated twice
     (17, 50304, 50304, "bf16", True, 0.0),      # a row of the full vocabulary
     (3, 140000, 140000, "bf16", False, 0.0),    # rows beyond what registers hold
 ]
