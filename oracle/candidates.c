@@ -51,7 +51,7 @@ static int64_t mod_i64(int64_t a, int64_t m) {
  * info[0] = number of distinct targets (classes marked by targets alone)
  * info[1] = need   (P - distinct; 0 when no negatives are drawn)
  * info[2] = draw   (window length; 0 when need == 0)
- * info[3] = next_offset (the sweep offset after this build)
+ * info[3] = next_offset (the sweep offset after this candidate set is drawn)
  * info[4] = 1 if the fallback (every s-th free class) supplied the negatives
  * info[5] = N, the number of labels that survive the remap (target and prefix
  *           positions that are >= 0)
