@@ -3,15 +3,17 @@
  * LM-head step (forward and backward) on AMD Instinct MI355X (gfx950).
  *
  * The method ("sampled_softmax.py", modded-nanogpt track_1_short, module
- * docstring): for one microbatch of T tokens with hidden states x [T, d], the
- * training cross-entropy is a softmax over a candidate set C of P classes that
- * every token shares, instead of over all V classes. C holds every class that is
- * a target somewhere in the microbatch plus negatives taken from the next window
- * of the sweep k * stride mod V (stride coprime to V, so the sweep is a
- * permutation). Logits are x @ W[C]^T; every target and prefix target is replaced
- * by its position in C, and a prefix target that is not in C becomes -1, a label
- * that contributes nothing. The gradient of W (the LM head, [V, d]) is dense, with
- * zeros outside C. P = 0 means the full softmax over all V classes.
+ * docstring): the T tokens of one microbatch (hidden states x [T, d]) all share
+ * one set C of P output classes, and the training cross-entropy normalises over
+ * C rather than over the whole vocabulary of V classes. C is the union of the
+ * distinct labels of the microbatch with filler classes ("negatives") read off a
+ * fixed cyclic order of the vocabulary, c_k = k * stride mod V (a permutation
+ * because gcd(stride, V) = 1), starting at a caller-chosen index. The kernels see
+ * C as a P-class vocabulary: logits x @ W[C]^T, labels given as indexes into C.
+ * A prefix label whose class did not make it into C gets index -1 and is skipped;
+ * such labels never add classes to C. The LM-head gradient covers all V rows and
+ * is zero on every row outside C. P = 0 selects the ordinary softmax over all V
+ * classes.
  *
  * Conventions shared by every entry point:
  *   - Every array pointer is a DEVICE pointer unless its comment says "host".
@@ -222,13 +224,16 @@ SCE_API sce_status sce_gather_rows(const void* W, int64_t V, int64_t d, const in
                                    int32_t* status_out, void* stream);
 
 /*
- * Stage timing for benchmarks. sce_profile_enable(1) makes every later call of
- * sampled_ce_forward_backward record a HIP event on its stream at each stage
- * boundary (up to 512 calls; later calls are not timed); sce_profile_enable(0)
- * stops it. sce_profile_collect waits for the recorded events, writes into
- * stage_ms (HOST array of at least SCE_NUM_STAGES doubles) the milliseconds each
- * stage took summed over the timed calls, stores the number of calls in *ncalls
- * (HOST, may be NULL) and forgets them. Process-wide state: not thread-safe.
+ * Stage timing for benchmarks. sce_profile_enable(1) creates the HIP events it
+ * needs on the current device (once; the only resources the library ever creates,
+ * kept until the process ends) and makes every later call of the step entry points
+ * record one of them on its stream at each stage boundary (up to 512 calls; later
+ * calls are not timed); sce_profile_enable(0) stops it. A step call itself creates
+ * nothing. sce_profile_collect waits for the recorded events, writes into stage_ms
+ * (HOST array of at least SCE_NUM_STAGES doubles) the milliseconds each stage took
+ * summed over the timed calls, stores the number of calls in *ncalls (HOST, may be
+ * NULL) and forgets them. Process-wide state: enable and collect must not run
+ * concurrently with each other or with timed calls.
  */
 enum {
   SCE_STAGE_CANDIDATES = 0, /* candidate build, label remap and the row gather of W[C] */

@@ -8,10 +8,10 @@
  * no code, header or constant with the HIP sources.
  *
  * Source: "sampled_softmax.py" (modded-nanogpt, track_1_short course mirror):
- *   - module docstring: C = every class that is a target in the microbatch, plus
- *     negatives from the next window of the sweep k*stride mod V, which is a
- *     permutation because stride and V are coprime; a prefix target that is not
- *     in C maps to position -1 and never adds a class to C;
+ *   - module docstring: C is the set of distinct labels of the microbatch topped
+ *     up with filler classes from a window of the cyclic order k*stride mod V (a
+ *     permutation since gcd(stride, V) = 1); prefix labels only look classes up
+ *     in C (position -1 when absent) and never add one;
  *   - CandidateBuilder.__init__ / reset: the sweep and its offset into it;
  *   - CandidateBuilder._negatives: window length, window advance, the fallback;
  *   - CandidateBuilder.build: marking, the distinct-count check, ascending C,
@@ -79,7 +79,7 @@ int oracle_build_candidates(int64_t V, int64_t P, int64_t stride, int64_t offset
       return ORC_TARGET_RANGE;
   }
 
-  /* Mark every class that is a target somewhere in the microbatch. */
+  /* One mark per class that occurs as a label (a target) in this microbatch. */
   unsigned char* mark = (unsigned char*)calloc((size_t)V, 1);
   if (mark == NULL) return ORC_NO_MEMORY;
   for (int64_t t = 0; t < T; ++t)

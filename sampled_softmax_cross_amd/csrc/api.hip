@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/sampled_ce.h"
 #include "common.h"
 #include "kernels.h"
@@ -117,25 +119,24 @@ sce_status check_sizes(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bo
 sce_status hip_status(hipError_t e) { return e == hipSuccess ? SCE_OK : SCE_EHIP; }
 
 // Optional stage timing: when enabled, every call records a HIP event on its
-// stream at each stage boundary; sce_profile_collect() sums the elapsed times.
+// stream at each stage boundary; sce_profile_collect() sums the elapsed times. The
+// events are created by sce_profile_enable (never inside a step call); a call claims
+// its slot with one atomic increment.
 constexpr int kMaxProfiledCalls = 512;
 struct Profile {
-  bool on = false;
-  int calls = 0;
+  std::atomic<bool> on{false};
+  std::atomic<int> calls{0};
+  int device = -1;  // the device the events were created on
   hipEvent_t ev[kMaxProfiledCalls][SCE_NUM_STAGES + 1] = {};
-  bool created[kMaxProfiledCalls] = {};
 } g_prof;
 
 struct StageMarks {
   int call = -1;
   hipStream_t s;
   explicit StageMarks(hipStream_t stream) : s(stream) {
-    if (!g_prof.on || g_prof.calls >= kMaxProfiledCalls) return;
-    call = g_prof.calls++;
-    if (!g_prof.created[call]) {
-      for (int i = 0; i <= SCE_NUM_STAGES; ++i) (void)hipEventCreate(&g_prof.ev[call][i]);
-      g_prof.created[call] = true;
-    }
+    if (!g_prof.on.load(std::memory_order_acquire)) return;
+    const int c = g_prof.calls.fetch_add(1, std::memory_order_relaxed);
+    if (c < kMaxProfiledCalls) call = c;
   }
   // Marks the boundary before stage `i` (i == SCE_NUM_STAGES: after the last).
   void mark(int i) {
@@ -462,15 +463,33 @@ sce_status sce_gather_rows(const void* W, int64_t V, int64_t d, const int32_t* i
 }
 
 sce_status sce_profile_enable(int on) {
-  if (on && !g_prof.on) g_prof.calls = 0;  // a new timing window; disabling keeps the record
-  g_prof.on = on != 0;
+  if (on && !g_prof.on.load()) {
+    // a new timing window; the events are made once, on the current device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SCE_EHIP;
+    if (g_prof.device != dev) {
+      for (int c = 0; c < kMaxProfiledCalls; ++c)
+        for (int i = 0; i <= SCE_NUM_STAGES; ++i) {
+          if (g_prof.device >= 0) (void)hipEventDestroy(g_prof.ev[c][i]);
+          if (hipEventCreate(&g_prof.ev[c][i]) != hipSuccess) {
+            g_prof.device = -1;
+            return SCE_EHIP;
+          }
+        }
+      g_prof.device = dev;
+    }
+    g_prof.calls.store(0);
+  }
+  g_prof.on.store(on != 0, std::memory_order_release);  // disabling keeps the record
   return SCE_OK;
 }
 
 sce_status sce_profile_collect(double* stage_ms, int nstages, int* ncalls) {
   if (stage_ms == nullptr || nstages < SCE_NUM_STAGES) return SCE_EINVAL;
   for (int i = 0; i < nstages; ++i) stage_ms[i] = 0.0;
-  for (int c = 0; c < g_prof.calls; ++c) {
+  int n = g_prof.calls.load();
+  if (n > kMaxProfiledCalls) n = kMaxProfiledCalls;
+  for (int c = 0; c < n; ++c) {
     if (hipEventSynchronize(g_prof.ev[c][SCE_NUM_STAGES]) != hipSuccess) return SCE_EHIP;
     for (int i = 0; i < SCE_NUM_STAGES; ++i) {
       float ms = 0.f;
@@ -479,8 +498,8 @@ sce_status sce_profile_collect(double* stage_ms, int nstages, int* ncalls) {
       stage_ms[i] += ms;
     }
   }
-  if (ncalls) *ncalls = g_prof.calls;
-  g_prof.calls = 0;
+  if (ncalls) *ncalls = n;
+  g_prof.calls.store(0);
   return SCE_OK;
 }
 

@@ -574,6 +574,9 @@ hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
 hipError_t launch_ce_rows_g8(const void* Z, int64_t ldz, int T, int P, const int32_t* target_pos,
                              const int32_t* prefix_pos, const int32_t* counters, float* row_loss,
                              float* row_lse, const G8Out& go, hipStream_t s) {
+  // the kernels write the codes of columns [0, ldz) (zeros past P) in rows ldg apart; a
+  // wider pitch would leave bytes the e4m3 products read unwritten
+  if (go.ldg != ldz || ldz % 16 != 0) return hipErrorInvalidValue;
   if (T <= 0) return hipGetLastError();
   launch_ce_typed<bf16_t, true>(static_cast<bf16_t*>(const_cast<void*>(Z)), ldz, T, P, target_pos,
                                 prefix_pos, const_cast<int32_t*>(counters), row_loss, row_lse, go, s);

@@ -166,8 +166,10 @@ hipError_t launch_ce_rows(void* Z, int64_t ldz, int T, int P, bool bf16,
 // e4m3 step: the same over bf16 Z, with the gradient written as e4m3 codes of g / s_g
 // to its own buffer (Z is left as it is) and s_g derived from N.
 struct G8Out {
-  uint8_t* g8;        // [T, ldg] codes; columns [P, ldg) are not written
-  int64_t ldg;        // a multiple of 16, >= ldz
+  uint8_t* g8;        // [T, ldg] codes; every column below ldz is written, those in
+                      // [P, ldz) as zero codes: the e4m3 products read 16-element chunks
+                      // that straddle K = P and rely on those zeros
+  int64_t ldg;        // equal to ldz (a multiple of 16; checked by the launcher)
   int n_max;          // labels per row at most: 1, or 2 with prefix targets
   float* scales;      // the step's scale table (reads kScaleX, kScaleW; writes the rest)
   float* scales_out;  // caller's {s_x, s_g}, or null (writes [1])
