@@ -111,6 +111,33 @@ SCE_API sce_status sce_build_candidates(const int64_t* targets, const int64_t* p
                                 void* stream);
 
 /*
+ * sce_build_candidates_noalloc -- sce_build_candidates with no workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Arguments, results and error
+ * behaviour are those of sce_build_candidates. Its scratch (the counters, the
+ * candidate bitmap and per-word prefix counts, and the prefix positions when
+ * prefix_pos_out is NULL) lives in one static device array of
+ * SCE_NOALLOC_SCRATCH_BYTES bytes per GPU, loaded with the library and held until the
+ * process ends; the call allocates and frees nothing. The first call on a device looks
+ * up that device's copy of the array (with that device current).
+ *   Returns SCE_EWORKSPACE, before enqueuing anything, when the sizes need more scratch
+ *   than the array holds: about 37 KB of fixed pieces for V <= SCE_MAX_V_SAMPLED, plus
+ *   4 * T bytes when prefix_pos_out is NULL (so T up to about 250000 then; any T when
+ *   prefix_pos_out is given).
+ *   Every call on a GPU uses that GPU's one array, which keeps the last call's
+ *   contents (each call rewrites what it reads): calls that overlap in time on one GPU
+ *   (other streams, other threads) race and give wrong results. Order them.
+ */
+#define SCE_NOALLOC_SCRATCH_BYTES (1 << 20)
+SCE_API sce_status sce_build_candidates_noalloc(const int64_t* targets,
+                                                const int64_t* prefix_targets, int64_t T,
+                                                int64_t V, int64_t P, int64_t stride,
+                                                int64_t offset, int32_t* candidates_out,
+                                                int32_t* vocab_pos_out, int32_t* target_pos_out,
+                                                int32_t* prefix_pos_out, int64_t* aux_out,
+                                                void* stream);
+
+/*
  * sampled_ce_forward_backward -- the whole step: candidate build (as above),
  * gather W_C = W[C], logits Z = x W_C^T (fp32 accumulation, stored in dtype),
  * per row the log-sum-exp L_t = max_j Z + ln sum_j exp(Z - max), the loss

@@ -19,7 +19,8 @@ DEV_TOO_MANY_TARGETS, DEV_LABEL_RANGE, DEV_SCALE_RANGE = 1, 2, 4
 MAX_V_SAMPLED, MAX_V, MAX_D = 131072, 1048576, 16384
 STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
 
-EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sampled_ce_forward_backward",
+EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sce_build_candidates_noalloc",
+           "sampled_ce_forward_backward",
            "sampled_ce_forward_backward_fp8",
            "sce_ce_rows_workspace_size", "sce_ce_rows", "sce_gather_rows",
            "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
@@ -49,6 +50,8 @@ def load_library(path: str = LIB_PATH):
     lib.sce_workspace_size.restype = i32
     lib.sce_build_candidates.argtypes = [p, p, i64, i64, i64, i64, i64, p, p, p, p, p, p, sz, p]
     lib.sce_build_candidates.restype = i32
+    lib.sce_build_candidates_noalloc.argtypes = [p, p, i64, i64, i64, i64, i64, p, p, p, p, p, p]
+    lib.sce_build_candidates_noalloc.restype = i32
     lib.sampled_ce_forward_backward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                                 p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.sampled_ce_forward_backward.restype = i32
@@ -135,6 +138,29 @@ def build_candidates(targets, prefix_targets, V, P, stride, offset, *, want_voca
     if rc != 0:
         raise SceError("sce_build_candidates", rc)
     return dict(C=C, target_pos=tpos[:T], prefix_pos=ppos[:T], vocab_pos=vpos, aux=aux)
+
+
+def build_candidates_noalloc(targets, prefix_targets, V, P, stride, offset, *,
+                             want_vocab_pos=False, want_prefix_pos=True):
+    """The candidate build with the library's static scratch instead of a workspace
+    (sce_build_candidates_noalloc). Same results as build_candidates; with
+    want_prefix_pos=False no prefix positions are returned (the library keeps them in its
+    scratch). Calls on one GPU must not overlap in time."""
+    lib = load_library()
+    dev = targets.device
+    T = targets.shape[0]
+    C = torch.empty(P, dtype=torch.int32, device=dev)
+    tpos = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    ppos = torch.empty(max(T, 1), dtype=torch.int32, device=dev) if want_prefix_pos else None
+    vpos = torch.empty(V, dtype=torch.int32, device=dev) if want_vocab_pos else None
+    aux = torch.empty(4, dtype=torch.int64, device=dev)
+    rc = lib.sce_build_candidates_noalloc(_ptr(targets), _ptr(prefix_targets), T, V, P, stride,
+                                          offset, _ptr(C), _ptr(vpos), _ptr(tpos), _ptr(ppos),
+                                          _ptr(aux), _stream(dev))
+    if rc != 0:
+        raise SceError("sce_build_candidates_noalloc", rc)
+    return dict(C=C, target_pos=tpos[:T], prefix_pos=None if ppos is None else ppos[:T],
+                vocab_pos=vpos, aux=aux)
 
 
 def forward_backward(x, W, targets, prefix_targets, P, stride, offset, *, outputs=None, ws=None,

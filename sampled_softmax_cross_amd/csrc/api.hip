@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/sampled_ce.h"
 #include "common.h"
@@ -144,6 +145,89 @@ struct StageMarks {
   }
 };
 
+// Argument checks shared by both candidate-build entry points.
+sce_status check_build_args(const int64_t* targets, int64_t T, int64_t V, int64_t P,
+                            int64_t stride, const int32_t* candidates_out,
+                            const int32_t* target_pos_out) {
+  const sce_status st = check_sizes(T, 8, V, P, SCE_F32, false);
+  if (st != SCE_OK || P < 1) return SCE_EINVAL;
+  if ((T > 0 && (targets == nullptr || target_pos_out == nullptr)) || candidates_out == nullptr)
+    return SCE_EINVAL;
+  if (gcd64(mod64(stride, V), V) != 1) return SCE_EINVAL;
+  return SCE_OK;
+}
+
+// The candidate build's launches, given its scratch: counters, the candidate bitmap and
+// per-word prefix counts (ceil(V/32) words each), and prefix positions [T] used when the
+// caller passes none.
+hipError_t enqueue_build(const int64_t* targets, const int64_t* prefix_targets, int64_t T,
+                         int64_t V, int64_t P, int64_t stride, int64_t offset,
+                         int32_t* candidates_out, int32_t* vocab_pos_out, int32_t* target_pos_out,
+                         int32_t* prefix_pos_out, int64_t* aux_out, int32_t* counters,
+                         uint32_t* bits, int32_t* wpre, int32_t* ppos_scratch, hipStream_t hs) {
+  int32_t* ppos = prefix_pos_out ? prefix_pos_out : ppos_scratch;
+  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P,
+                                   (int)mod64(stride, V), (int)mod64(offset, V), counters,
+                                   candidates_out, bits, wpre, vocab_pos_out, target_pos_out, ppos,
+                                   nullptr, 0, nullptr, 0, nullptr, 0, hs);
+  if (e == hipSuccess && aux_out) e = launch_write_aux(counters, aux_out, hs);
+  return e;
+}
+
+// Layout of the no-allocation build's scratch: the counters, the bitmap and prefix
+// counts, then (only when the caller passes no prefix_pos_out) prefix positions [T].
+struct NoAllocPlan {
+  size_t counters = 0, bits = 0, wpre = 0, ppos = 0, total = 0;
+};
+NoAllocPlan make_noalloc_plan(int64_t T, int64_t V, bool need_ppos) {
+  NoAllocPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  p.counters = take(kCounterWords * sizeof(int32_t));
+  p.bits = take((size_t)((V + 31) / 32) * sizeof(uint32_t));
+  p.wpre = take((size_t)((V + 31) / 32) * sizeof(int32_t));
+  p.ppos = need_ppos ? take((size_t)(T > 0 ? T : 1) * sizeof(int32_t)) : 0;
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+}  // namespace sce
+
+// Scratch of sce_build_candidates_noalloc: one copy per GPU, held until the process
+// ends. Host code never passes this name to a kernel or a copy (on the host it stands for
+// no device address): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device by noalloc_scratch().
+static __device__ __align__(256) unsigned char scratch[SCE_NOALLOC_SCRATCH_BYTES];
+
+namespace sce {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (looked up on its first use
+// on that device, with that device current).
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 }  // namespace
 }  // namespace sce
 
@@ -178,27 +262,40 @@ sce_status sce_build_candidates(const int64_t* targets, const int64_t* prefix_ta
                                 int32_t* target_pos_out, int32_t* prefix_pos_out,
                                 int64_t* aux_out, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  sce_status st = check_sizes(T, 8, V, P, SCE_F32, false);
-  if (st != SCE_OK || P < 1) return SCE_EINVAL;
-  if ((T > 0 && (targets == nullptr || target_pos_out == nullptr)) || candidates_out == nullptr)
-    return SCE_EINVAL;
-  const int64_t s = mod64(stride, V);
-  if (gcd64(s, V) != 1) return SCE_EINVAL;
+  const sce_status st = check_build_args(targets, T, V, P, stride, candidates_out, target_pos_out);
+  if (st != SCE_OK) return st;
   const Plan p = make_plan(T, 8, V, P, SCE_F32, false);
   if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
-  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
-  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
-  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), counters, candidates_out, bits, wpre,
-                                   vocab_pos_out, target_pos_out, ppos, nullptr, 0, nullptr, 0,
-                                   nullptr, 0, hs);
-  if (e == hipSuccess && aux_out) e = launch_write_aux(counters, aux_out, hs);
-  return hip_status(e);
+  return hip_status(enqueue_build(targets, prefix_targets, T, V, P, stride, offset, candidates_out,
+                                  vocab_pos_out, target_pos_out, prefix_pos_out, aux_out,
+                                  reinterpret_cast<int32_t*>(ws + p.counters),
+                                  reinterpret_cast<uint32_t*>(ws + p.bits),
+                                  reinterpret_cast<int32_t*>(ws + p.wpre),
+                                  reinterpret_cast<int32_t*>(ws + p.ppos),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+sce_status sce_build_candidates_noalloc(const int64_t* targets, const int64_t* prefix_targets,
+                                        int64_t T, int64_t V, int64_t P, int64_t stride,
+                                        int64_t offset, int32_t* candidates_out,
+                                        int32_t* vocab_pos_out, int32_t* target_pos_out,
+                                        int32_t* prefix_pos_out, int64_t* aux_out, void* stream) {
+  const sce_status st = check_build_args(targets, T, V, P, stride, candidates_out, target_pos_out);
+  if (st != SCE_OK) return st;
+  const NoAllocPlan p = make_noalloc_plan(T, V, prefix_pos_out == nullptr);
+  if (p.total > (size_t)SCE_NOALLOC_SCRATCH_BYTES) return SCE_EWORKSPACE;
+  void* base = nullptr;
+  if (noalloc_scratch(&base) != hipSuccess) return SCE_EHIP;
+  char* ws = static_cast<char*>(base);
+  return hip_status(enqueue_build(targets, prefix_targets, T, V, P, stride, offset, candidates_out,
+                                  vocab_pos_out, target_pos_out, prefix_pos_out, aux_out,
+                                  reinterpret_cast<int32_t*>(ws + p.counters),
+                                  reinterpret_cast<uint32_t*>(ws + p.bits),
+                                  reinterpret_cast<int32_t*>(ws + p.wpre),
+                                  reinterpret_cast<int32_t*>(ws + p.ppos),
+                                  static_cast<hipStream_t>(stream)));
 }
 
 sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64_t* targets,

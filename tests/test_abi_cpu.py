@@ -155,3 +155,17 @@ def test_fp8_host_checks(lib):
     assert g(fake, fake, fake, None, 4, 16, 16, 4, 3, 0, binding.SCE_E4M3, fake, fake, fake, None, None,
              None, None, None, None, None, 0, None) == 1  # the e4m3 step has its own entry point
 
+
+
+def test_noalloc_build_host_checks(lib):
+    """The scratch limit and the argument checks of sce_build_candidates_noalloc are
+    decided on the host, before the scratch is looked up or anything is enqueued."""
+    f = lib.sce_build_candidates_noalloc
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails on the host
+    # prefix positions kept in the scratch: 4 bytes per token beyond the fixed pieces
+    big_T = (1 << 20) // 4
+    assert f(fake, fake, big_T, 50304, 10240, 20011, 0, fake, None, fake, None, None, None) == 2
+    assert f(fake, fake, 100, 50304, 0, 20011, 0, fake, None, fake, None, None, None) == 1   # P = 0
+    assert f(fake, fake, 100, 50304, 10, 2, 0, fake, None, fake, None, None, None) == 1      # gcd != 1
+    assert f(fake, fake, 100, 131073, 10, 1, 0, fake, None, fake, None, None, None) == 1     # V too large
+    assert f(fake, None, 100, 500, 10, 7, 0, None, None, fake, None, None, None) == 1        # no C output
