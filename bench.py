@@ -7,10 +7,14 @@ logits GEMM, fused CE forward/backward, dX and dW GEMMs, dense scatter, over one
 microbatch of synthetic inputs already resident in HBM. --dtype e4m3 times
 sampled_ce_forward_backward_fp8 on the same microbatch instead (the lm_head as an
 e4m3 cache with one scale, x quantised per call, e4m3 products). Prints ONE JSON line:
-tokens/s of the whole step, the roofline fraction of its dominant kernel (timed
-live with HIP events the library records on the call's stream), the same library
-at P = V for the speedup of the sampled path, and the CPU oracle on a bounded
-sample of the same workload.
+tokens/s of the whole step on the headline workload (stage-0/1, P = 10240), the
+roofline fraction of its dominant kernel (timed live with HIP events the library
+records on the call's stream), the same library at P = V for the speedup of the
+sampled path, the other configurations the metric names (P = 14336 and 24576 at
+T = 49152, and the full softmax) with theirs, and the CPU oracle on a bounded sample
+of the headline workload. Every measurement follows ~100 ms of untimed steps
+(`settle_steps`), so it sees the GPU's settled clock rather than the transient right
+after an idle period.
 """
 import argparse
 import json
@@ -83,6 +87,168 @@ def recorded_traffic(workload, stage, e4m3=False):
     return int(s["fetch_bytes"] + s["write_bytes"])
 
 
+OTHER_CONFIGS = ("s2early", "s2late", "full")
+
+
+def stage_table(stage_ms, work, ptype):
+    """Per-stage times with the achieved rate and its fraction of the published peak."""
+    stages = {}
+    for k, t in stage_ms.items():
+        entry = {"ms": round(t, 5)}
+        if k in work and t > 0.01:
+            kind, amount = work[k]
+            if kind == "mfma":
+                ach = amount / (t * 1e-3) / 1e12
+                entry.update(tflops=round(ach, 2), frac=round(ach / PEAK_TFLOPS[ptype], 4))
+            else:
+                ach = amount / (t * 1e-3) / 1e9
+                entry.update(gbs=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 4))
+        stages[k] = entry
+    return stages
+
+
+def roofline_of(w, stage_ms, work, ptype, e4m3):
+    """The dominant (slowest) kernel's algorithmic rate against its published peak."""
+    dom = max((k for k in work if k in stage_ms), key=lambda k: stage_ms[k])
+    kind, amount = work[dom]
+    traffic = recorded_traffic(w.name, dom, e4m3)
+    if kind == "mfma":
+        achieved = amount / (stage_ms[dom] * 1e-3) / 1e12
+        return {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_TFLOPS[ptype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[ptype], 4), "traffic": traffic}
+    achieved = amount / (stage_ms[dom] * 1e-3) / 1e9
+    return {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+class Bench:
+    """One workload resident on the GPU, and the measurements of its step."""
+
+    def __init__(self, w, dev, e4m3):
+        import numpy as np
+        import torch
+
+        from sampled_softmax_cross_amd import synth
+
+        self.w, self.dev, self.e4m3 = w, dev, e4m3
+        self.torch = torch
+        x, W = synth.make_weights(w)
+        self.host = (x, W)
+
+        def to_dev(a):
+            if w.dtype == "bf16":
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a).to(dev)
+
+        self.xd, self.Wd = to_dev(x), to_dev(W)
+        # one label set per consecutive call of the workload (the 4-call workload advances
+        # its candidate offset by P per call; a step takes the calls in turn)
+        self.calls = []
+        for c in range(w.calls):
+            y, p = synth.make_labels(w, c)
+            if c == 0:
+                self.labels0 = (y, p)
+            self.calls.append((torch.from_numpy(y).to(dev),
+                               torch.from_numpy(p).to(dev) if p is not None else None,
+                               w.call_offset(c)))
+        self.i = 0
+        self.outs = {}
+        if e4m3:
+            self.W8, self.w_scale = synth.e4m3_cache(W)
+            self.W8d = torch.from_numpy(self.W8).to(dev)
+
+    def step(self, P, outputs=None, ws=None):
+        from sampled_softmax_cross_amd import binding
+
+        w = self.w
+        yd, pd, off = self.calls[self.i % len(self.calls)]
+        self.i += 1
+        o = self.outs.get(P) if outputs is None else outputs
+        if self.e4m3:
+            return binding.forward_backward_fp8(self.xd, self.W8d, self.w_scale, yd, pd, P,
+                                                w.stride, off, outputs=o, ws=ws)
+        return binding.forward_backward(self.xd, self.Wd, yd, pd, P, w.stride, off, outputs=o,
+                                        ws=ws)
+
+    def prepare(self, P):
+        self.outs[P] = self.step(P)  # outputs and workspace allocated once
+        self.torch.cuda.synchronize()
+
+    def settle(self, P, ms=100.0):
+        """Untimed steps for about `ms` milliseconds: after an idle period the GPU's clock
+        overshoots and settles over the first ~25 steps (measured at stage-0/1: steps 5..25
+        after 2 s idle 8% slower than the steady state), and every later measurement should
+        see the steady state a training loop runs in. Returns the number of steps run."""
+        torch = self.torch
+        n, t0 = 0, time.perf_counter()
+        while n < 4 or (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(4):
+                self.step(P)
+            torch.cuda.synchronize()
+            n += 4
+        return n
+
+    def timed(self, P, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(P)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s.record()
+        for _ in range(steps):
+            self.step(P)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps, time.perf_counter() - t0
+
+    def stage_ms(self, P, n):
+        """Per-stage times from HIP events the library records on the call's stream."""
+        from sampled_softmax_cross_amd import binding
+
+        binding.profile_enable(True)
+        for _ in range(n):
+            self.step(P)
+        binding.profile_enable(False)
+        tot, ncalls = binding.profile_collect()
+        return {k: v / ncalls for k, v in tot.items()}
+
+    def graph_ms(self, P, reps):
+        """The same call captured once in a HIP graph and replayed."""
+        from sampled_softmax_cross_amd import binding
+
+        torch, w = self.torch, self.w
+        code = binding.SCE_E4M3 if self.e4m3 else binding.dtype_code(self.xd.dtype)
+        ws = binding.workspace(binding.workspace_size(w.T, w.d, w.V, P, code), self.dev)
+        o = self.outs[P]
+        i0 = self.i
+        call = lambda: self.step(P, outputs=o, ws=ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.i = i0
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        gms = _time_ms(g.replay, reps=reps, warmup=3)
+        del g
+        return gms
+
+    def check_status(self, P):
+        aux = self.outs[P]["aux"].cpu().tolist()
+        if aux[3] != 0:
+            raise RuntimeError(f"device status {aux[3]} in the {self.w.name} step")
+
+    def release(self):
+        self.outs.clear()
+        self.torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +260,9 @@ def main():
                          "operand step on the same bf16 microbatch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only the headline workload (not the other configurations the "
+                         "metric names)")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the measured reference peaks (device copy, library GEMM)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
@@ -110,132 +279,36 @@ def main():
               "batch is the unit measured here", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from sampled_softmax_cross_amd import binding, synth
+    from sampled_softmax_cross_amd import synth
 
     if args.micro:
         micro(args.micro)
         return
-    w = synth.workload(args.workload)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"[bench] workload {w.name}: T={w.T} d={w.d} V={w.V} P={w.P} {w.dtype}")
-    x, W = synth.make_weights(w)
-    y, p = synth.make_labels(w, 0)
-
-    def to_dev(a):
-        if w.dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
     e4m3 = args.dtype == "e4m3"
+    w = synth.workload(args.workload)
     if e4m3 and w.dtype != "bf16":
         raise SystemExit("--dtype e4m3 needs a bf16 workload")
-    xd, Wd = to_dev(x), to_dev(W)
-    yd = torch.from_numpy(y).to(dev)
-    pd = torch.from_numpy(p).to(dev) if p is not None else None
-    off = w.offset
-    outs = {}
-    if e4m3:
-        W8, w_scale = synth.e4m3_cache(W)
-        W8d = torch.from_numpy(W8).to(dev)
-        log(f"[bench] e4m3 products: lm_head cache scale {w_scale:.4g}")
-
-    def step(P):
-        if e4m3:
-            return binding.forward_backward_fp8(xd, W8d, w_scale, yd, pd, P, w.stride, off,
-                                                outputs=outs.get(P))
-        return binding.forward_backward(xd, Wd, yd, pd, P, w.stride, off, outputs=outs.get(P))
-
-    def timed(P, steps, warmup):
-        outs[P] = step(P)  # allocate outputs and workspace once
-        for _ in range(warmup):
-            step(P)
-        torch.cuda.synchronize()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        s.record()
-        for _ in range(steps):
-            step(P)
-        e.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return s.elapsed_time(e) / steps, wall
-
-    ms, wall = timed(w.P, args.steps, args.warmup)
-
-    def graph_ms(P, reps):
-        """The same call captured once in a HIP graph and replayed (the launches of
-        the step without host-side launch overhead)."""
-        code = binding.SCE_E4M3 if e4m3 else binding.dtype_code(xd.dtype)
-        ws = binding.workspace(binding.workspace_size(w.T, w.d, w.V, P, code), dev)
-        o = outs[P]
-        if e4m3:
-            call = lambda: binding.forward_backward_fp8(xd, W8d, w_scale, yd, pd, P, w.stride, off,
-                                                        outputs=o, ws=ws)
-        else:
-            call = lambda: binding.forward_backward(xd, Wd, yd, pd, P, w.stride, off, outputs=o,
-                                                    ws=ws)
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            call()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            call()
-        gms = _time_ms(g.replay, reps=reps, warmup=3)
-        del g
-        return gms
-
-    gms = graph_ms(w.P, max(20, min(args.steps, 200)))
-    log(f"[bench] as a replayed HIP graph: {gms:.4f} ms/step ({w.T / gms * 1e3 / 1e6:.2f} M tokens/s)")
-    aux = outs[w.P]["aux"].cpu().tolist()
-    if aux[3] != 0:
-        raise RuntimeError(f"device status {aux[3]} in the benchmark step")
-    log(f"[bench] {ms:.4f} ms/step ({w.T / ms * 1e3 / 1e6:.2f} M tokens/s); wall {wall:.3f} s")
-
-    # per-stage times from HIP events recorded by the library on the call's stream
-    binding.profile_enable(True)
-    nprof = max(10, min(args.steps, 50))
-    for _ in range(nprof):
-        step(w.P)
-    binding.profile_enable(False)
-    stage_ms, ncalls = binding.profile_collect()
-    stage_ms = {k: v / ncalls for k, v in stage_ms.items()}
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ptype = "e4m3" if e4m3 else w.dtype
+    log(f"[bench] workload {w.name}: T={w.T} d={w.d} V={w.V} P={w.P} {ptype}")
+    b = Bench(w, dev, e4m3)
+    b.prepare(w.P)
     P_eff = w.P if w.P else w.V
     work = stage_work(w, P_eff, e4m3)
-    ptype = "e4m3" if e4m3 else w.dtype
-    stages = {}
-    for k, t in stage_ms.items():
-        entry = {"ms": round(t, 5)}
-        if k in work and t > 0.01:
-            kind, amount = work[k]
-            if kind == "mfma":
-                ach = amount / (t * 1e-3) / 1e12
-                entry.update(tflops=round(ach, 2), frac=round(ach / PEAK_TFLOPS[ptype], 4))
-            else:
-                ach = amount / (t * 1e-3) / 1e9
-                entry.update(gbs=round(ach, 1), frac=round(ach / PEAK_HBM_GBS, 4))
-        stages[k] = entry
+    settled = b.settle(w.P)
+    log(f"[bench] {settled} untimed steps while the clock settles")
+    stage_ms = b.stage_ms(w.P, max(20, min(args.steps, 50)))
+    stages = stage_table(stage_ms, work, ptype)
     log("[bench] stages: " + json.dumps(stages))
-    dom = max((k for k in work if k in stage_ms), key=lambda k: stage_ms[k])
-    kind, amount = work[dom]
-    if kind == "mfma":
-        achieved = amount / (stage_ms[dom] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK_TFLOPS[ptype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS[ptype], 4),
-                "traffic": recorded_traffic(w.name, dom, e4m3)}
-    else:
-        achieved = amount / (stage_ms[dom] * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic(w.name, dom, e4m3)}
+    roof = roofline_of(w, stage_ms, work, ptype, e4m3)
+    gms = b.graph_ms(w.P, max(20, min(args.steps, 200)))
+    log(f"[bench] as a replayed HIP graph: {gms:.4f} ms/step ({w.T / gms * 1e3 / 1e6:.2f} M tokens/s)")
+    ms, wall = b.timed(w.P, args.steps, args.warmup)
+    b.check_status(w.P)
+    log(f"[bench] {ms:.4f} ms/step ({w.T / ms * 1e3 / 1e6:.2f} M tokens/s); wall {wall:.3f} s")
 
     if args.calibrate_copy_mib:
         src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -248,17 +321,27 @@ def main():
 
     achievable = None if args.no_achievable else measured_peaks(torch, dev, ptype)
     if achievable:
-        ref = achievable["gemm_tflops"] if kind == "mfma" else achievable["copy_gbs"]
+        ref = achievable["gemm_tflops"] if roof["bound"] == "mfma" else achievable["copy_gbs"]
         achievable["dominant_frac"] = round(roof["achieved"] / ref, 4)
         log(f"[bench] achievable on this GPU: {achievable}")
 
     full_cmp = None
     if not args.no_full_compare and w.P > 0:
-        ms_v, _ = timed(w.V, max(5, args.steps // 5), 2)
+        b.prepare(w.V)
+        ms_v, _ = b.timed(w.V, max(5, args.steps // 5), 2)
         full_cmp = {"P": w.V, "ms_per_step": round(ms_v, 4), "speedup": round(ms_v / ms, 3)}
         log(f"[bench] same library at P=V: {ms_v:.4f} ms/step -> sampled speedup {ms_v / ms:.2f}x")
-        del outs[w.V]
-        torch.cuda.empty_cache()
+    x, W = b.host
+    y, p = b.labels0
+    b.release()
+    del b
+
+    others = None
+    if not args.no_other_configs and args.workload == "stage01":
+        others = {}
+        for name in OTHER_CONFIGS:
+            others[name] = other_config(synth.workload(name), dev, e4m3, args, torch)
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -279,17 +362,52 @@ def main():
         "dtype": ptype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "V": w.V, "P": w.P,
-                   "stride": w.stride, "offset": off, "targets": f"zipf({w.zipf_s})",
+                   "stride": w.stride, "offset": w.offset, "targets": f"zipf({w.zipf_s})",
                    "prefix_targets": w.prefix,
                    **({"operands": "e4m3 x and lm_head, bf16 logits"} if e4m3 else {})},
         "roofline": roof,
         "achievable": achievable,
+        "settle_steps": settled,
         "graph_replay": {"ms_per_step": round(gms, 5), "value": round(w.T / (gms * 1e-3), 1)},
         "stages": stages,
         "full_softmax_same_library": full_cmp,
+        "other_configs": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def other_config(w, dev, e4m3, args, torch):
+    """The step on another configuration the metric names, in the same order of
+    measurement (stage timing, then the timed steps), with its dominant kernel's roofline
+    and, for a sampled configuration, the same library at P = V on the same microbatch."""
+    ptype = "e4m3" if e4m3 else w.dtype
+    log(f"[bench] workload {w.name}: T={w.T} d={w.d} V={w.V} P={w.P} {ptype}")
+    b = Bench(w, dev, e4m3)
+    b.prepare(w.P)
+    P_eff = w.P if w.P else w.V
+    work = stage_work(w, P_eff, e4m3)
+    settled = b.settle(w.P)
+    stage_ms = b.stage_ms(w.P, 12)
+    stages = stage_table(stage_ms, work, ptype)
+    roof = roofline_of(w, stage_ms, work, ptype, e4m3)
+    steps = max(8, args.steps // 2)
+    ms, _ = b.timed(w.P, steps, max(4, args.warmup))
+    b.check_status(w.P)
+    res = {"T": w.T, "P": w.P, "calls": w.calls, "settle_steps": settled, "steps": steps,
+           "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(w.T / (ms * 1e-3), 1), "roofline": roof, "stages": stages}
+    log(f"[bench]   {ms:.4f} ms/step ({w.T / ms * 1e3 / 1e6:.2f} M tokens/s); dominant {roof['kernel']} "
+        f"at {roof['frac']:.3f} of peak")
+    if w.P > 0 and not args.no_full_compare:
+        b.release()
+        b.prepare(w.V)
+        ms_v, _ = b.timed(w.V, max(4, steps // 2), 2)
+        res["full_softmax_same_library"] = {"P": w.V, "ms_per_step": round(ms_v, 4),
+                                            "speedup": round(ms_v / ms, 3)}
+        log(f"[bench]   same library at P=V: {ms_v:.4f} ms/step -> {ms_v / ms:.2f}x")
+    b.release()
+    return res
 
 
 def measured_peaks(torch, dev, ptype):
@@ -400,12 +518,10 @@ def micro(kind):
 
 
 def cpu_baseline(w, x, W, y, p, sample_tokens, e4m3=False):
-    """The float64 CPU oracle, as it stands, on the first `sample_tokens` tokens of the
-    same microbatch: candidate build + dense loss and gradients (the e4m3 oracle for the
-    e4m3 step)."""
-    from threadpoolctl import threadpool_info
-
-    from oracle import build_candidates, ce, fp8
+    """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the same
+    microbatch: candidate build (plain C) + dense loss and gradients (plain C, float64,
+    OpenMP over token blocks; for the e4m3 step the float64 numpy e4m3 oracle)."""
+    from oracle import build_candidates, ce_c, fp8
     from sampled_softmax_cross_amd import synth
 
     Ts = min(sample_tokens, w.T)
@@ -421,15 +537,19 @@ def cpu_baseline(w, x, W, y, p, sample_tokens, e4m3=False):
     ppos = cand["prefix_pos"] if ps is not None else None
     if e4m3:
         fp8.forward_backward(xs, W8, w_scale, C, cand["target_pos"], ppos)
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        kind = "float64 numpy e4m3 oracle (BLAS threads)"
     else:
-        ce.forward_backward(xs, Wf, C, cand["target_pos"], ppos)
+        ce_c.forward_backward(xs, Wf, C, cand["target_pos"], ppos)
+        threads = ce_c.threads()
+        kind = "plain C float64 oracle, OpenMP over token blocks"
     dt = time.perf_counter() - t0
-    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     return {"value": round(Ts / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "nproc": os.cpu_count(), "seconds": round(dt, 2),
             "sample": f"first {Ts} of {w.T} tokens of the {w.name} microbatch (same P, V, d, "
-                      f"stride, offset): candidate build + float64 loss, dX, dW"
-                      + (" of the e4m3 step" if e4m3 else "")}
+                      f"stride, offset; C built from these tokens): candidate build + loss, dX, "
+                      f"dW by the {kind}"}
 
 
 if __name__ == "__main__":

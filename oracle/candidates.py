@@ -26,7 +26,7 @@ def _load():
     global _lib
     if _lib is None:
         path = _build.LIB
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+        if _build.stale():
             _build.build(force=True)
         lib = ctypes.CDLL(path)
         p = ctypes.c_void_p

@@ -159,8 +159,10 @@ def dx_rows(x, WC, L, target_pos, prefix_pos, N, rows):
     return (g / N) @ WC
 
 
-def dwc_rows(x, WC, L, target_pos, prefix_pos, N, cand_rows, block=256):
-    """dW_C[j] for the given candidate positions j: sum over tokens of g[t, j] x[t]."""
+def dwc_rows(x, WC, L, target_pos, prefix_pos, N, cand_rows, block=256, tblock=8192):
+    """dW_C[j] for the given candidate positions j: sum over tokens of g[t, j] x[t].
+    Columns are taken `block` at a time and tokens `tblock` at a time, only to bound
+    memory."""
     cand_rows = np.asarray(cand_rows, dtype=np.int64)
     d = WC.shape[1]
     out = np.zeros((cand_rows.shape[0], d))
@@ -173,13 +175,14 @@ def dwc_rows(x, WC, L, target_pos, prefix_pos, N, cand_rows, block=256):
         j = cand_rows[s:s + block]
         T = x.shape[0]
         acc = np.zeros((j.shape[0], d))
-        for t0 in range(0, T, 8192):
-            xb = np.asarray(x[t0:t0 + 8192], dtype=np.float64)
+        for t0 in range(0, T, tblock):
+            t1 = t0 + tblock
+            xb = np.asarray(x[t0:t1], dtype=np.float64)
             zc = xb @ WC[j].T                                  # [tb, |j|]
-            g = n[t0:t0 + 8192, None] * np.exp(zc - L[t0:t0 + 8192, None])
-            g -= (tpos[t0:t0 + 8192, None] == j[None, :])
+            g = n[t0:t1, None] * np.exp(zc - L[t0:t1, None])
+            g -= (tpos[t0:t1, None] == j[None, :])
             if ppos is not None:
-                g -= (ppos[t0:t0 + 8192, None] == j[None, :])
+                g -= (ppos[t0:t1, None] == j[None, :])
             acc += g.T @ xb
         out[s:s + block] = acc / N
     return out

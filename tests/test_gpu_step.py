@@ -7,9 +7,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import build_candidates, ce
+from oracle import build_candidates, ce_c
 from sampled_softmax_cross_amd import binding, synth
-from tests.gpu_util import TOL, inputs_f64, labels_dev, max_rel, to_dev, to_f64
+from tests.gpu_util import TOL, inputs_f64, labels_dev, max_rel, max_row_rel, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_step_matches_oracle(T, d, V, P, dtype, prefix, ign, stride):
     xf, Wf = inputs_f64(x, W, dtype)
     C = None if P == 0 else cand["C"]
     ppos = cand["prefix_pos"] if p is not None else None
-    loss, dX, dW, L, row_loss = ce.forward_backward(xf, Wf, C, cand["target_pos"], ppos)
+    loss, dX, dW, L, row_loss = ce_c.forward_backward(xf, Wf, C, cand["target_pos"], ppos)
     tol = TOL[dtype]
     # integers: exact
     if P > 0:
@@ -75,6 +75,21 @@ def test_step_matches_oracle(T, d, V, P, dtype, prefix, ign, stride):
     gX, gW = to_f64(out["dX"]), to_f64(out["dW"])
     assert max_rel(gX, dX) <= tol["grad"], max_rel(gX, dX)
     assert max_rel(gW, dW) <= tol["grad"], max_rel(gW, dW)
+    # row by row: every dX row and every candidate row of dW whose largest entry is at
+    # least 1e-3 of the tensor's, held to its own magnitude. This applies while the logits
+    # stay within |z| <= 8 (every workload shape: |z| <~ 3 at d = 768): beyond that the
+    # logits' own rounding (bf16: 2^-9 |z|; fp32: the product's accumulation over K = d)
+    # moves 1 - softmax of a confident row by more than the tolerance's share, and the
+    # d = 16384 cases (|z| up to ~20) keep the tensor-wide measure only.
+    cls = np.arange(V) if C is None else C
+    per_row = z_max.max() <= 8.0
+    for name, g, r in (("dX", gX, dX), ("dW", gW[cls], dW[cls])):
+        worst, n = max_row_rel(g, r)
+        print(f"  {name}: {n} rows, worst row max-rel {worst:.2e}"
+              f"{'' if per_row else ' (max|z| %.1f: tensor-wide measure only)' % z_max.max()}",
+              flush=True)
+        if per_row:
+            assert worst <= tol["grad"], (name, worst)
     if P > 0:
         outside = np.setdiff1d(np.arange(V), cand["C"])
         raw = out["dW"].cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy()

@@ -1,10 +1,13 @@
 """Pins for the float64 loss/gradient oracle (CPU only).
 
-The oracle follows the definitions stated in its module header. It is tied here
-to things other than itself: the handout's worked example (loss = ln 5 at a zero
-table, a zero gradient row, hand-worked gradient entries), the handout's
-token-weighted accumulation check, PyTorch's own cross-entropy and autograd in
-float64, central finite differences, and closed forms.
+The oracle has two implementations of the same definition: plain C with OpenMP
+(oracle/ce.c through oracle/ce_c.py, the one the GPU tests and the benchmark's CPU
+baseline use) and float64 numpy (oracle/ce.py). Every pin below runs on both (the
+`impl` fixture). They are tied here to things other than themselves: the handout's
+worked example (loss = ln 5 at a zero table, a zero gradient row, hand-worked gradient
+entries), the handout's token-weighted accumulation check, PyTorch's own
+cross-entropy and autograd in float64, central finite differences, closed forms, and
+each other at sizes that run every block loop of the full-size helpers more than once.
 """
 import json
 import math
@@ -15,8 +18,14 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import build_candidates, ce
+from oracle import build_candidates, ce, ce_c
 from sampled_softmax_cross_amd import synth
+
+
+@pytest.fixture(params=["c", "numpy"])
+def impl(request):
+    """The oracle implementation under test: plain C (ce_c) or numpy (ce)."""
+    return ce_c if request.param == "c" else ce
 
 
 def _lm_case(golden_dir):
@@ -29,11 +38,11 @@ def _lm_case(golden_dir):
 
 
 @pytest.mark.parametrize("P", [0, 5])
-def test_handout_worked_example(golden_dir, P):
+def test_handout_worked_example(golden_dir, P, impl):
     g, x, y = _lm_case(golden_dir)
     W = np.zeros((5, 5))
     C = None if P == 0 else build_candidates(5, P, 2, 0, y)["C"]
-    loss, dX, dW, L, _ = ce.forward_backward(x, W, C, y)
+    loss, dX, dW, L, _ = impl.forward_backward(x, W, C, y)
     assert math.isclose(loss, math.log(5), rel_tol=0, abs_tol=1e-15)
     table_grad = np.array([[float(Fraction(v)) for v in row] for row in g["table_grad"]])
     np.testing.assert_allclose(dW.T, table_grad, rtol=0, atol=1e-16)
@@ -42,16 +51,16 @@ def test_handout_worked_example(golden_dir, P):
     assert ce.num_labels(y, None) == g["N"]
 
 
-def test_handout_token_weighted_accumulation(golden_dir):
+def test_handout_token_weighted_accumulation(golden_dir, impl):
     """Full-batch loss/gradient == per-document sums each divided by the total target
     count, at the handout's non-uniform table sin(0..24)."""
     _, x, y = _lm_case(golden_dir)
     W = np.sin(np.arange(25, dtype=np.float64)).reshape(5, 5).T.copy()
-    loss, dX, dW, _, _ = ce.forward_backward(x, W, None, y)
+    loss, dX, dW, _, _ = impl.forward_backward(x, W, None, y)
     N = ce.num_labels(y, None)
     acc_loss, acc_dW, acc_dX = 0.0, np.zeros_like(dW), []
     for doc in (slice(0, 4), slice(4, 8)):
-        l_i, dX_i, dW_i, _, _ = ce.forward_backward(x[doc], W, None, y[doc])
+        l_i, dX_i, dW_i, _, _ = impl.forward_backward(x[doc], W, None, y[doc])
         n_i = ce.num_labels(y[doc], None)
         acc_loss += l_i * n_i / N
         acc_dW += dW_i * n_i / N
@@ -62,7 +71,7 @@ def test_handout_token_weighted_accumulation(golden_dir):
     # a per-document mean (the handout's wrong variant) gives a different gradient
     wrong = np.zeros_like(dW)
     for doc in (slice(0, 4), slice(4, 8)):
-        _, _, dW_i, _, _ = ce.forward_backward(x[doc], W, None, y[doc])
+        _, _, dW_i, _, _ = impl.forward_backward(x[doc], W, None, y[doc])
         wrong += dW_i * ce.num_labels(y[doc], None) / (ce.num_labels(y[doc], None) * 2)
     assert not np.allclose(wrong, dW)
 
@@ -92,13 +101,13 @@ def _torch_reference(x, W, C, tpos, ppos):
     (3, 17, 5, 12, 7, False, 0.3),
     (4, 128, 64, 512, 256, True, 0.0),
 ])
-def test_matches_torch_cross_entropy(seed, T, d, V, P, prefix, ign):
+def test_matches_torch_cross_entropy(seed, T, d, V, P, prefix, ign, impl):
     x, W, y, p = synth.small_case(seed, T, d, V, "f32", prefix=prefix, ignore_frac=ign)
     x, W = x.astype(np.float64), W.astype(np.float64)
     cand = build_candidates(V, P, 7 if math.gcd(7, V) == 1 else 11, seed, y, p)
     C = None if P == 0 else cand["C"]
     tpos, ppos = cand["target_pos"], (cand["prefix_pos"] if prefix else None)
-    loss, dX, dW, L, row_loss = ce.forward_backward(x, W, C, tpos, ppos)
+    loss, dX, dW, L, row_loss = impl.forward_backward(x, W, C, tpos, ppos)
     r_loss, r_dX, r_dW = _torch_reference(x, W, C, tpos, ppos)
     assert math.isclose(loss, r_loss, rel_tol=1e-12)
     np.testing.assert_allclose(dX, r_dX, rtol=1e-10, atol=1e-14)
@@ -142,7 +151,7 @@ def test_ce_rows_matches_torch_on_logits(seed, T, P, prefix, ign):
     assert math.isclose(row_loss.sum() / n, loss, rel_tol=1e-12)
 
 
-def test_central_finite_differences():
+def test_central_finite_differences(impl):
     """d loss / d x and d loss / d W against central differences (h = 1e-6), with a
     duplicated label (prefix == target), a dropped prefix and an ignored target."""
     rng = np.random.default_rng(11)
@@ -156,9 +165,9 @@ def test_central_finite_differences():
     assert (ppos == -1).sum() >= 2 and tpos[0] == ppos[0]
 
     def f(xx, WW):
-        return ce.forward_backward(xx, WW, C, tpos, ppos)[0]
+        return impl.forward_backward(xx, WW, C, tpos, ppos)[0]
 
-    _, dX, dW, _, _ = ce.forward_backward(x, W, C, tpos, ppos)
+    _, dX, dW, _, _ = impl.forward_backward(x, W, C, tpos, ppos)
     h = 1e-6
     for arr, grad, which in ((x, dX, 0), (W, dW, 1)):
         num = np.zeros_like(arr)
@@ -174,7 +183,7 @@ def test_central_finite_differences():
 
 
 @pytest.mark.parametrize("P", [2048, 0])
-def test_closed_forms(P):
+def test_closed_forms(P, impl):
     V, T, d = 4096, 64, 16
     x, W, y, p = synth.small_case(5, T, d, V, "f32", prefix=True, ignore_frac=0.1)
     x, W = x.astype(np.float64), W.astype(np.float64)
@@ -182,42 +191,42 @@ def test_closed_forms(P):
     C = None if P == 0 else cand["C"]
     Peff = V if P == 0 else P
     # x = 0: every logit is 0, so each label costs ln P and dW = g^T x = 0
-    loss, dX, dW, L, _ = ce.forward_backward(np.zeros_like(x), W, C, cand["target_pos"], cand["prefix_pos"])
+    loss, dX, dW, L, _ = impl.forward_backward(np.zeros_like(x), W, C, cand["target_pos"], cand["prefix_pos"])
     assert math.isclose(loss, math.log(Peff), rel_tol=1e-14)
     assert (dW == 0).all()
     # W = 0: same loss, dX = g W_C = 0
-    loss, dX, dW, _, _ = ce.forward_backward(x, np.zeros_like(W), C, cand["target_pos"], cand["prefix_pos"])
+    loss, dX, dW, _, _ = impl.forward_backward(x, np.zeros_like(W), C, cand["target_pos"], cand["prefix_pos"])
     assert math.isclose(loss, math.log(Peff), rel_tol=1e-14)
     assert (dX == 0).all()
 
 
-def test_gradient_rows_sum_to_zero_and_no_labels():
+def test_gradient_rows_sum_to_zero_and_no_labels(impl):
     V, T, d = 300, 40, 8
     x, W, y, p = synth.small_case(6, T, d, V, "f32", prefix=True)
     x, W = x.astype(np.float64), W.astype(np.float64)
     cand = build_candidates(V, 120, 7, 3, y, p)
     C = cand["C"]
-    _, dX, dW, L, _ = ce.forward_backward(x, W, C, cand["target_pos"], cand["prefix_pos"])
+    _, dX, dW, L, _ = impl.forward_backward(x, W, C, cand["target_pos"], cand["prefix_pos"])
     # sum over candidates of g[t, j] is zero for every row, so sum_j dW_C[j] = 0
     np.testing.assert_allclose(dW[C].sum(axis=0), 0.0, atol=1e-14)
     # N = 0: loss and gradients are zero
     none = np.full(T, -1, dtype=np.int64)
-    loss, dX, dW, _, _ = ce.forward_backward(x, W, C, none, none)
+    loss, dX, dW, _, _ = impl.forward_backward(x, W, C, none, none)
     assert loss == 0.0 and (dX == 0).all() and (dW == 0).all()
 
 
-def test_noop_prefix_equals_no_prefix_and_p_equals_v():
+def test_noop_prefix_equals_no_prefix_and_p_equals_v(impl):
     V, T, d = 256, 50, 8
     x, W, y, _ = synth.small_case(7, T, d, V, "f32", prefix=False)
     x, W = x.astype(np.float64), W.astype(np.float64)
     cand = build_candidates(V, 100, 7, 0, y)
-    a = ce.forward_backward(x, W, cand["C"], cand["target_pos"], None)
-    b = ce.forward_backward(x, W, cand["C"], cand["target_pos"], np.full(T, -1))
+    a = impl.forward_backward(x, W, cand["C"], cand["target_pos"], None)
+    b = impl.forward_backward(x, W, cand["C"], cand["target_pos"], np.full(T, -1))
     for u, v in zip(a, b):
         assert np.array_equal(np.asarray(u), np.asarray(v))
-    full = ce.forward_backward(x, W, None, y, None)
+    full = impl.forward_backward(x, W, None, y, None)
     pv = build_candidates(V, V, 7, 0, y)
-    same = ce.forward_backward(x, W, pv["C"], pv["target_pos"], None)
+    same = impl.forward_backward(x, W, pv["C"], pv["target_pos"], None)
     for u, v in zip(full, same):
         assert np.array_equal(np.asarray(u), np.asarray(v))
 
@@ -239,3 +248,65 @@ def test_sampled_helpers_match_dense():
     np.testing.assert_allclose(ce.dx_rows(x, WC, L2, tpos, ppos, N, rows), dX[rows], rtol=1e-10, atol=1e-15)
     js = np.array([0, 1, 200, 399])
     np.testing.assert_allclose(ce.dwc_rows(x, WC, L2, tpos, ppos, N, js), dW[C[js]], rtol=1e-10, atol=1e-15)
+
+
+def test_full_size_helpers_run_every_block_loop_twice():
+    """The entry-by-entry helpers the full-size GPU parity tests rest on, at a size where
+    each of their block loops runs more than once with its default block sizes (numpy:
+    8192-token and 256-column blocks of dwc_rows, 2048-row blocks of lse_rows; C: 64-token
+    and 64-column blocks), against the dense numpy forms and each other."""
+    V, T, d, P = 2000, 9000, 16, 320
+    x, W, y, p = synth.small_case(21, T, d, V, "f32", prefix=True, ignore_frac=0.05)
+    x, W = x.astype(np.float64), W.astype(np.float64)
+    y = np.where(y >= 0, y % 250, -1)      # at most 250 distinct targets for P = 320
+    cand = build_candidates(V, P, 7, 123, y, p)
+    C, tpos, ppos = cand["C"], cand["target_pos"], cand["prefix_pos"]
+    loss, dX, dW, L, row_loss = ce.forward_backward(x, W, C, tpos, ppos)
+    WC = W[C]
+    N = cand["N"]
+    rows = np.array([0, 1, 2047, 2048, 8191, 8192, 8999])   # both sides of every block edge
+    cols = np.arange(P)                                       # 2 numpy blocks, 5 C blocks
+    # numpy helpers
+    L_np = ce.lse_rows(x, WC)
+    np.testing.assert_allclose(L_np, L, rtol=1e-13)
+    l_np, r_np, N_np = ce.loss_from_lse(x, WC, L_np, tpos, ppos)
+    assert math.isclose(l_np, loss, rel_tol=1e-12) and N_np == N
+    np.testing.assert_allclose(r_np, row_loss, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ce.dx_rows(x, WC, L_np, tpos, ppos, N, rows), dX[rows], rtol=1e-10,
+                               atol=1e-15)
+    np.testing.assert_allclose(ce.dwc_rows(x, WC, L_np, tpos, ppos, N, cols), dW[C], rtol=1e-10,
+                               atol=1e-15)
+    # the same with blocks small enough for many iterations (ragged last blocks)
+    np.testing.assert_allclose(ce.dwc_rows(x, WC, L_np, tpos, ppos, N, cols, block=37, tblock=1001),
+                               dW[C], rtol=1e-10, atol=1e-15)
+    # C helpers, every row and column
+    L_c = ce_c.lse_rows(x, W, C)
+    np.testing.assert_allclose(L_c, L, rtol=1e-13)
+    l_c, r_c, N_c = ce_c.loss_from_lse(x, W, C, L_c, tpos, ppos)
+    assert math.isclose(l_c, loss, rel_tol=1e-12) and N_c == N
+    np.testing.assert_allclose(r_c, row_loss, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ce_c.dx_rows(x, W, C, L_c, tpos, ppos, N), dX, rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(ce_c.dx_rows(x, W, C, L_c, tpos, ppos, N, rows), dX[rows], rtol=1e-10,
+                               atol=1e-15)
+    np.testing.assert_allclose(ce_c.dwc_rows(x, W, C, L_c, tpos, ppos, N), dW[C], rtol=1e-10,
+                               atol=1e-15)
+    np.testing.assert_allclose(ce_c.dwc_rows(x, W, C, L_c, tpos, ppos, N, cols[::-7]),
+                               dW[C[cols[::-7]]], rtol=1e-10, atol=1e-15)
+
+
+def test_c_oracle_rejects_out_of_range_indexes():
+    """Rows, columns and label positions outside their ranges are refused before any
+    access (the C oracle never reads out of bounds)."""
+    x = np.zeros((4, 8))
+    W = np.zeros((10, 8))
+    C = np.array([1, 3, 5], dtype=np.int32)
+    t = np.array([0, 2, -1, 1], dtype=np.int32)
+    with pytest.raises(ce_c.OracleCeError):
+        ce_c.lse_rows(x, W, C, rows=[0, 4])
+    L = ce_c.lse_rows(x, W, C)
+    with pytest.raises(ce_c.OracleCeError):
+        ce_c.dwc_rows(x, W, C, L, t, None, 3, cand_rows=[3])
+    with pytest.raises(ce_c.OracleCeError):
+        ce_c.loss_from_lse(x, W, C, L, np.array([0, 3, -1, 1]), None)
+    with pytest.raises(ValueError):
+        ce_c.lse_rows(x, W, np.array([1, 10]))

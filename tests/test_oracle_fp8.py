@@ -219,3 +219,37 @@ def test_row_helpers_agree_with_dense():
     np.testing.assert_allclose(
         fp8.dwc_rows(xv, WCv, s_xw, L, tpos, ppos, dense["N"], dense["s_g"], dense["s_x"], cols),
         dense["dW"][C[cols]], rtol=1e-13, atol=1e-18)
+
+
+def test_full_size_helpers_run_every_block_loop_twice():
+    """fp8.lse_rows (2048-row blocks) and fp8.dwc_rows (8192-token blocks), and the
+    full-size bounds (fp8_tol.sampled_bounds, 2048-row blocks) against their dense forms
+    (fp8.forward_backward, fp8_tol.step_bounds) at T = 9000, where every loop runs
+    more than once."""
+    from tests import fp8_tol
+
+    x, W8, w_scale, C, tpos, ppos = _tiny(seed=22, T=9000, d=32, V=700, P=320, with_prefix=True,
+                                          full=False)
+    dense = fp8.forward_backward(x, W8, w_scale, C, tpos, ppos)
+    WCv = fp8.e4m3_decode(W8[C])
+    xv = fp8.e4m3_decode(dense["x8"])
+    s_xw = dense["s_x"] * float(np.float32(w_scale))
+    L = fp8.lse_rows(xv, WCv, s_xw)
+    np.testing.assert_allclose(L, dense["L"], rtol=1e-14)
+    cols = np.arange(0, 320, 3)
+    np.testing.assert_allclose(
+        fp8.dwc_rows(xv, WCv, s_xw, L, tpos, ppos, dense["N"], dense["s_g"], dense["s_x"], cols),
+        dense["dW"][C[cols]], rtol=1e-13, atol=1e-18)
+    rows = np.array([0, 2047, 2048, 8191, 8192, 8999])
+    np.testing.assert_allclose(
+        fp8.dx_rows(xv, WCv, s_xw, L, tpos, ppos, dense["N"], dense["s_g"], w_scale, rows),
+        dense["dX"][rows], rtol=1e-13, atol=1e-18)
+    full = fp8_tol.step_bounds(dense, dense["x8"], W8[C], w_scale, C, tpos, ppos)
+    samp = fp8_tol.sampled_bounds(dense["x8"], W8[C], w_scale, dense["s_x"], dense["s_g"], dense["N"],
+                                  tpos, ppos, dense["L"], rows, cols, dense["dX"][rows],
+                                  dense["dW"][C[cols]], dense["row_loss"], dense["loss"])
+    np.testing.assert_allclose(samp["row_lse"], full["row_lse"], rtol=1e-12, atol=0)
+    np.testing.assert_allclose(samp["dX"], full["dX"][rows], rtol=1e-12, atol=0)
+    np.testing.assert_allclose(samp["dWC"], full["dWC"][cols], rtol=1e-12, atol=0)
+    assert samp["loss"] == pytest.approx(full["loss"], rel=1e-12)
+    assert full["dX"].min() > 0 and full["dWC"].min() > 0 and full["loss"] > 0
