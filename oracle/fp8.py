@@ -126,6 +126,30 @@ def quantize_x(x):
     return e4m3_encode(x / s), s
 
 
+def cache_scale(amax):
+    """The e4m3 cache's scale for a weight tensor whose largest magnitude is amax (a
+    float32 value): float32(amax / 448), the largest magnitude landing on e4m3's largest
+    finite value; 1.0 when amax == 0. The float64 quotient rounded to float32 is the
+    correctly rounded float32 quotient (double rounding of a quotient through a format
+    with at least 2p + 2 bits, 53 >= 2 * 24 + 2, is innocuous: Figueroa, "When is double
+    rounding innocuous?", SIGNUM Newsletter 1995)."""
+    s = np.float32(np.float64(np.float32(amax)) / E4M3_MAX)
+    return 1.0 if s == 0 else float(s)
+
+
+def e4m3_cache(W):
+    """The lm_head's e4m3 cache ("sampled_softmax.py" keeps the weights as a float8_e4m3fn
+    copy, refreshed before the candidate rows are gathered; the page does not give the
+    encoding, the reading here is one per-tensor scale): W [V, d] float64 values (exact
+    widenings of bf16 or float32 weights). Returns (codes uint8 [V, d], s_w) with
+    s_w = cache_scale(max|W|) and codes = e4m3 of the float32 quotient W / s_w (the
+    correctly rounded float32 division, by the same double-rounding argument)."""
+    W = np.asarray(W, dtype=np.float64)
+    s_w = cache_scale(np.abs(W).max() if W.size else 0.0)
+    q = (W / s_w).astype(np.float32).astype(np.float64)
+    return e4m3_encode(q), s_w
+
+
 def forward_backward(x, W8, w_scale, C, target_pos, prefix_pos=None):
     """Dense fp8 oracle. x [T,d] float64 (exact widening of the bf16 input), W8 [V,d]
     e4m3 codes, w_scale the float32 dequantisation scale, C the candidate classes

@@ -253,3 +253,84 @@ def test_full_size_helpers_run_every_block_loop_twice():
     np.testing.assert_allclose(samp["dWC"], full["dWC"][cols], rtol=1e-12, atol=0)
     assert samp["loss"] == pytest.approx(full["loss"], rel=1e-12)
     assert full["dX"].min() > 0 and full["dWC"].min() > 0 and full["loss"] > 0
+
+
+# ---------------------------------------------------------------------------
+# The e4m3 lm_head cache (scale max|W| / 448, codes of the float32 quotient)
+# ---------------------------------------------------------------------------
+
+def _bf_f32_quotient(a, b):
+    """Nearest float32 (normal range) of the exact rational a / b, ties to even."""
+    q = Fraction(a) / Fraction(b)
+    if q == 0:
+        return 0.0
+    m = abs(q)
+    e = 0
+    while m >= 2:
+        m /= 2
+        e += 1
+    while m < 1:
+        m *= 2
+        e -= 1
+    step = Fraction(2) ** (e - 23)                  # 24 significant bits
+    lo = (abs(q) // step) * step
+    hi = lo + step
+    dl, dh = abs(q) - lo, hi - abs(q)
+    r = lo if dl < dh or (dl == dh and (lo / step) % 2 == 0) else hi
+    return float(r) if q > 0 else -float(r)
+
+
+def _bf16_values(seed, shape, scale):
+    v = np.random.default_rng(seed).standard_normal(shape) * scale
+    return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_cache_matches_torch_cast():
+    """Scale and codes against torch: float32 max / 448 and the float8_e4m3fn cast of the
+    float32 quotient, all in torch's float32 arithmetic."""
+    for seed, shape, sc in ((3, (513, 64), 0.02), (4, (97, 48), 3.0), (5, (64, 16), 1e-3)):
+        W = _bf16_values(seed, shape, sc)
+        Wt = torch.from_numpy(W.astype(np.float32))
+        s_ref = (Wt.abs().max() / torch.tensor(448.0, dtype=torch.float32)).item()
+        codes_ref = (Wt / torch.tensor(s_ref, dtype=torch.float32)).to(torch.float8_e4m3fn)
+        codes, s = fp8.e4m3_cache(W)
+        assert s == s_ref
+        assert np.array_equal(codes, codes_ref.view(torch.uint8).numpy())
+
+
+def test_cache_brute_force():
+    """Tiny tensors: the scale by exact rational rounding to float32, each code by
+    exhaustive nearest-code search over the exactly rounded float32 quotient."""
+    for seed in range(4):
+        W = _bf16_values(10 + seed, (5, 16), 10.0 ** (seed - 2))
+        amax = float(np.abs(W).max())
+        s = _bf_f32_quotient(amax, 448)
+        codes, s_o = fp8.e4m3_cache(W)
+        assert s_o == s
+        ref = np.array([[_bf_encode(_bf_f32_quotient(v, s)) for v in row] for row in W], np.uint8)
+        assert np.array_equal(codes, ref)
+
+
+def test_cache_values_fixed_by_the_definition():
+    # all zeros: scale 1, every code +0
+    codes, s = fp8.e4m3_cache(np.zeros((4, 16)))
+    assert s == 1.0 and not codes.any()
+    # the largest magnitude lands on +-448 (0x7e / 0xfe) whatever its value
+    W = _bf16_values(20, (33, 32), 0.7)
+    i = np.unravel_index(np.abs(W).argmax(), W.shape)
+    codes, s = fp8.e4m3_cache(W)
+    assert codes[i] == (0xFE if W[i] < 0 else 0x7E)
+    assert np.all(np.abs(fp8.e4m3_decode(codes)) <= 448)
+    # values that are e4m3 values times 2^k, with 448 2^k present, come back unchanged
+    rng = np.random.default_rng(21)
+    c = rng.choice([c for c in range(256) if (c & 0x7F) != 0x7F], size=(16, 32)).astype(np.uint8)
+    c[3, 5] = 0xFE
+    for k in (-12, 0, 7):
+        codes, s = fp8.e4m3_cache(fp8.e4m3_decode(c) * 2.0 ** k)
+        assert s == 2.0 ** k and np.array_equal(codes, c)
+    # error bound: |s_w decode(code) - W| <= half an e4m3 step of W / s_w, times s_w
+    W = _bf16_values(22, (64, 64), 0.05)
+    codes, s = fp8.e4m3_cache(W)
+    q = np.abs(W / s)
+    step = np.where(q >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(q, 1e-300))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(fp8.e4m3_decode(codes) * s - W) <= 0.5 * step * s * (1 + 2.0 ** -20))
