@@ -4,9 +4,11 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage01] [--dtyp
 
 A step is one call of sampled_ce_forward_backward: candidate build, row gather,
 logits GEMM, fused CE forward/backward, dX and dW GEMMs, dense scatter, over one
-microbatch of synthetic inputs already resident in HBM. --dtype e4m3 times
-sampled_ce_forward_backward_fp8 on the same microbatch instead (the lm_head as an
-e4m3 cache with one scale, x quantised per call, e4m3 products). Prints ONE JSON line:
+microbatch of synthetic inputs already resident in HBM. --dtype e4m3 times, on the same
+microbatch, the lm_head's e4m3 cache refresh from the bf16 weights
+(sce_refresh_e4m3_cache, inside every timed step) followed by
+sampled_ce_forward_backward_fp8 reading the refreshed scale on the device (x quantised
+per call, e4m3 products). Prints ONE JSON line:
 tokens/s of the whole step on the headline workload (stage-0/1, P = 10240), the
 roofline fraction of its dominant kernel (timed live with HIP events the library
 records on the call's stream), the same library at P = V for the speedup of the
@@ -145,6 +147,7 @@ class Bench:
         # one label set per consecutive call of the workload (the 4-call workload advances
         # its candidate offset by P per call; a step takes the calls in turn)
         self.calls = []
+        self.host_calls = []
         for c in range(w.calls):
             y, p = synth.make_labels(w, c)
             if c == 0:
@@ -152,11 +155,17 @@ class Bench:
             self.calls.append((torch.from_numpy(y).to(dev),
                                torch.from_numpy(p).to(dev) if p is not None else None,
                                w.call_offset(c)))
+            self.host_calls.append((torch.from_numpy(y), torch.from_numpy(p) if p is not None else None,
+                                    w.call_offset(c)))
         self.i = 0
         self.outs = {}
         if e4m3:
-            self.W8, self.w_scale = synth.e4m3_cache(W)
-            self.W8d = torch.from_numpy(self.W8).to(dev)
+            from sampled_softmax_cross_amd import binding
+
+            # the lm_head's e4m3 cache, rebuilt from the bf16 weights on the device at the
+            # start of every step (the weights change at every optimizer step)
+            self.rws = torch.empty(binding.REFRESH_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+            self.cache = binding.refresh_e4m3_cache(self.Wd, ws=self.rws)
 
     def step(self, P, outputs=None, ws=None):
         from sampled_softmax_cross_amd import binding
@@ -166,10 +175,27 @@ class Bench:
         self.i += 1
         o = self.outs.get(P) if outputs is None else outputs
         if self.e4m3:
-            return binding.forward_backward_fp8(self.xd, self.W8d, self.w_scale, yd, pd, P,
-                                                w.stride, off, outputs=o, ws=ws)
+            self.refresh()
+            return binding.forward_backward_fp8(self.xd, self.cache["W8"], self.cache["w_scale"],
+                                                yd, pd, P, w.stride, off, outputs=o, ws=ws)
         return binding.forward_backward(self.xd, self.Wd, yd, pd, P, w.stride, off, outputs=o,
                                         ws=ws)
+
+    def refresh(self):
+        from sampled_softmax_cross_amd import binding
+
+        binding.refresh_e4m3_cache(self.Wd, outputs=self.cache, ws=self.rws)
+
+    def refresh_us(self, reps):
+        """The e4m3 cache refresh alone (microseconds per call), and its algorithmic HBM
+        rate: W read once (bf16) and the codes written once, 3 V d bytes."""
+        ms = _time_ms(self.refresh, reps=reps, warmup=3)
+        nbytes = 3.0 * self.w.V * self.w.d
+        if self.cache["status"].item() != 0:
+            raise RuntimeError("device status in the e4m3 cache refresh")
+        return {"us": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes": int(nbytes)}
 
     def prepare(self, P):
         self.outs[P] = self.step(P)  # outputs and workspace allocated once
@@ -203,6 +229,66 @@ class Bench:
         e.record()
         torch.cuda.synchronize()
         return s.elapsed_time(e) / steps, time.perf_counter() - t0
+
+    def pipelined_ms(self, steps, warmup):
+        """The step with its candidate build off the critical path, the way the page runs
+        it: while the GPU runs step i (sampled_ce_forward_backward_prebuilt), the host
+        builds the set of microbatch i + 1 (sce_build_candidates_host) into pinned memory
+        and a copy stream uploads it; step i + 1 waits only for that upload. Host and
+        device buffers are double-buffered and ordered by events. Returns ms per step
+        (bf16 / fp32 sampled steps)."""
+        from sampled_softmax_cross_amd import binding
+
+        torch, w = self.torch, self.w
+        main, copy = torch.cuda.current_stream(), torch.cuda.Stream()
+        T, P = w.T, w.P
+        pre = w.prefix
+
+        def slot(pin):
+            # one buffer per slot, so that one copy uploads the whole set: aux (int64 [4])
+            # first, then C, the target and the prefix positions
+            kw = dict(pin_memory=True) if pin else dict(device=self.dev)
+            buf = torch.empty(8 + P + (2 if pre else 1) * T, dtype=torch.int32, **kw)
+            return {"_buf": buf, "aux": buf[:8].view(torch.int64), "C": buf[8:8 + P],
+                    "target_pos": buf[8 + P:8 + P + T],
+                    "prefix_pos": buf[8 + P + T:8 + P + 2 * T] if pre else None}
+
+        host, devb = [slot(True), slot(True)], [slot(False), slot(False)]
+        copied = [torch.cuda.Event(), torch.cuda.Event()]
+        used = [torch.cuda.Event(), torch.cuda.Event()]
+        for e in used + copied:
+            e.record(main)
+        out = {"o": self.outs.get(P)}
+
+        def build_upload(i):
+            k = i % 2
+            y, p, off = self.host_calls[i % len(self.host_calls)]
+            copied[k].synchronize()  # the pinned slot's last upload has left it
+            binding.build_candidates_host(y, p, w.V, P, w.stride, off, outputs=host[k])
+            with torch.cuda.stream(copy):
+                copy.wait_event(used[k])  # the step that read the device slot is done
+                devb[k]["_buf"].copy_(host[k]["_buf"], non_blocking=True)
+                copied[k].record(copy)
+
+        def run(n, i0):
+            for i in range(i0, i0 + n):
+                main.wait_event(copied[i % 2])
+                out["o"] = binding.forward_backward_prebuilt(self.xd, self.Wd, devb[i % 2],
+                                                             outputs=out["o"])
+                used[i % 2].record(main)
+                build_upload(i + 1)  # on the host while the GPU runs step i
+
+        build_upload(0)
+        run(warmup, 0)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        run(steps, warmup)
+        e.record()
+        torch.cuda.synchronize()
+        if out["o"]["aux"][3].item() != 0:
+            raise RuntimeError("device status in the overlapped-build steps")
+        return s.elapsed_time(e) / steps
 
     def stage_ms(self, P, n):
         """Per-stage times from HIP events the library records on the call's stream."""
@@ -309,6 +395,20 @@ def main():
     ms, wall = b.timed(w.P, args.steps, args.warmup)
     b.check_status(w.P)
     log(f"[bench] {ms:.4f} ms/step ({w.T / ms * 1e3 / 1e6:.2f} M tokens/s); wall {wall:.3f} s")
+    refresh = None
+    if e4m3:
+        refresh = b.refresh_us(max(20, min(args.steps, 200)))
+        refresh["in_step"] = True
+        log(f"[bench] e4m3 cache refresh (inside every timed step): {refresh}")
+    pipelined = None
+    if w.P > 0 and not e4m3:
+        pms = b.pipelined_ms(args.steps, args.warmup)
+        pipelined = {"ms_per_step": round(pms, 5), "value": round(w.T / (pms * 1e-3), 1),
+                     "how": "next microbatch's candidate set built on the host "
+                            "(sce_build_candidates_host) and uploaded on a copy stream while the "
+                            "GPU runs the step from the current one "
+                            "(sampled_ce_forward_backward_prebuilt)"}
+        log(f"[bench] with the build overlapped: {pms:.4f} ms/step ({w.T / pms * 1e3 / 1e6:.2f} M tokens/s)")
 
     if args.calibrate_copy_mib:
         src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -364,11 +464,15 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "V": w.V, "P": w.P,
                    "stride": w.stride, "offset": w.offset, "targets": f"zipf({w.zipf_s})",
                    "prefix_targets": w.prefix,
-                   **({"operands": "e4m3 x and lm_head, bf16 logits"} if e4m3 else {})},
+                   **({"operands": "e4m3 x and lm_head, bf16 logits; the lm_head's e4m3 "
+                                   "cache refreshed from bf16 W on the device in every step"}
+                      if e4m3 else {})},
         "roofline": roof,
         "achievable": achievable,
         "settle_steps": settled,
         "graph_replay": {"ms_per_step": round(gms, 5), "value": round(w.T / (gms * 1e-3), 1)},
+        "build_overlapped": pipelined,
+        "e4m3_cache_refresh": refresh,
         "stages": stages,
         "full_softmax_same_library": full_cmp,
         "other_configs": others,
@@ -530,7 +634,7 @@ def cpu_baseline(w, x, W, y, p, sample_tokens, e4m3=False):
     ys = y[:Ts]
     ps = None if p is None else p[:Ts]
     if e4m3:
-        W8, w_scale = synth.e4m3_cache(W)
+        W8, w_scale = fp8.e4m3_cache(Wf)
     t0 = time.perf_counter()
     cand = build_candidates(w.V, w.P, w.stride, w.offset, ys, ps)
     C = None if w.P == 0 else cand["C"]

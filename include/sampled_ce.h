@@ -111,6 +111,23 @@ SCE_API sce_status sce_build_candidates(const int64_t* targets, const int64_t* p
                                 void* stream);
 
 /*
+ * sce_build_candidates_host -- the candidate build of sce_build_candidates on the host, for
+ * a caller that builds the next microbatch's set on a CPU thread while the GPU runs the
+ * current step and uploads it for sampled_ce_forward_backward_prebuilt, the way
+ * "sampled_softmax.py" does (CandidateBuilder runs with no device work on a worker thread;
+ * SampledSoftmax.prefetch / upload). Same arguments and results as sce_build_candidates,
+ * but every pointer is a HOST pointer, nothing is enqueued, and the call returns when the
+ * set is built. Device-detected conditions of the device build are reported the same way
+ * in aux_out[3] (which may be NULL). No workspace; the call allocates nothing and keeps no
+ * state, so calls from different threads are independent. V <= SCE_MAX_V_SAMPLED.
+ */
+SCE_API sce_status sce_build_candidates_host(const int64_t* targets, const int64_t* prefix_targets,
+                                             int64_t T, int64_t V, int64_t P, int64_t stride,
+                                             int64_t offset, int32_t* candidates_out,
+                                             int32_t* target_pos_out, int32_t* prefix_pos_out,
+                                             int64_t* aux_out);
+
+/*
  * sce_build_candidates_noalloc -- sce_build_candidates with no workspace argument, for
  * callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc. Arguments, results and error
@@ -175,6 +192,41 @@ SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, con
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * sampled_ce_forward_backward_prebuilt -- the same step from a candidate set built
+ * beforehand. "sampled_softmax.py" (CandidateBuilder docstring, SampledSoftmax.prefetch /
+ * upload / gather) builds the next microbatch's set off the step's critical path (on a
+ * worker thread, then uploads it) and only gathers rows in the step. Here the results of
+ * sce_build_candidates (or sce_build_candidates_noalloc) are the inputs, so a caller can
+ * run the next microbatch's build on another stream, with its own workspace and output
+ * arrays, while this step runs. The results are bit-identical to
+ * sampled_ce_forward_backward on the labels the set was built from.
+ *
+ *   x, W, T, d, V, dtype, loss, dX, dW, row_lse_out, row_loss_out: as in
+ *   sampled_ce_forward_backward (P >= 1 here: a sampled candidate set).
+ *   candidates  [P] int32: the set, strictly ascending classes in [0, V).
+ *   target_pos  [T] int32 in [-1, P); prefix_pos [T] int32 or NULL (= all -1).
+ *   build_aux   [4] int64 or NULL: the build's aux_out; its distinct count, next offset
+ *               and device bits are passed on.
+ *   aux_out     [4] int64 or NULL: {distinct (build_aux[0], or -1), N counted here from
+ *               the positions, next offset (build_aux[2], or -1), SCE_DEV_* bits}.
+ *   workspace   as for sampled_ce_forward_backward with the same sizes.
+ * The inputs are only read, and must not change until the step has run (stream order).
+ * A class out of range or out of order, or a position outside [-1, P), sets
+ * SCE_DEV_LABEL_RANGE; every access stays in bounds.
+ */
+SCE_API sce_status sampled_ce_forward_backward_prebuilt(const void* x, const void* W,
+                                                        const int32_t* candidates,
+                                                        const int32_t* target_pos,
+                                                        const int32_t* prefix_pos,
+                                                        const int64_t* build_aux, int64_t T,
+                                                        int64_t d, int64_t V, int64_t P,
+                                                        int dtype, float* loss, void* dX,
+                                                        void* dW, float* row_lse_out,
+                                                        float* row_loss_out, int64_t* aux_out,
+                                                        void* workspace, size_t workspace_bytes,
+                                                        void* stream);
+
+/*
  * sampled_ce_forward_backward_fp8 -- the same step with e4m3 (OCP E4M3, "e4m3fn")
  * matrix-product operands. "sampled_softmax.py" keeps the lm_head as an e4m3 cache,
  * gathers the candidate rows from it as e4m3 and multiplies with scaled fp8 products
@@ -191,7 +243,11 @@ SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, con
  * e4m3 encodings round to nearest, ties to even.
  *
  *   x [T, d] bf16, d a multiple of 16.    W8 [V, d] e4m3 codes (the lm_head cache).
- *   w_scale (host) > 0, finite: W ~ w_scale * W8.
+ *   w_scale (host) > 0, finite: W ~ w_scale * W8; used when w_scale_dev is NULL.
+ *   w_scale_dev (device float, or NULL): the cache's scale read on the device in stream
+ *         order (as sce_refresh_e4m3_cache writes it, with no host round trip); then
+ *         w_scale is ignored, and a value that is not positive and finite sets
+ *         SCE_DEV_SCALE_RANGE in aux_out[3].
  *   targets, prefix_targets, P, stride, offset, loss, the position outputs,
  *   row_lse_out, row_loss_out, aux_out: as in sampled_ce_forward_backward.
  *   dX [T, d], dW [V, d] bf16, overwritten.
@@ -200,6 +256,7 @@ SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, con
  * x non-finite, or with 0 < max|x| < 2^-100, sets SCE_DEV_SCALE_RANGE in aux_out[3].
  */
 SCE_API sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float w_scale,
+                                           const float* w_scale_dev,
                                            const int64_t* targets, const int64_t* prefix_targets,
                                            int64_t T, int64_t d, int64_t V, int64_t P,
                                            int64_t stride, int64_t offset, float* loss, void* dX,
@@ -208,6 +265,28 @@ SCE_API sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8
                                            float* row_lse_out, float* row_loss_out,
                                            int64_t* aux_out, float* scales_out, void* workspace,
                                            size_t workspace_bytes, void* stream);
+
+/*
+ * sce_refresh_e4m3_cache -- rebuilds the e4m3 lm_head cache the fp8 step reads from the
+ * bf16 weights ("sampled_softmax.py" refreshes this cache before it gathers candidate
+ * rows; the page does not give the encoding). Per-tensor scale, the largest magnitude
+ * mapped to e4m3's largest finite value 448:
+ *   s_w = float32( max|W| / 448 )  (1 when W is all zeros),
+ *   W8  = e4m3( float32(W / s_w) ) (correctly rounded float32 quotient, then round to
+ *         nearest even: the codes of torch's float8_e4m3fn cast of that quotient).
+ *   W [V, d] bf16 (device), d a multiple of 16, 16-byte aligned; V <= SCE_MAX_V.
+ *   W8_out [V, d] e4m3 codes (device, 16-byte aligned), overwritten.
+ *   w_scale_out: one device float, overwritten with s_w; pass it to the fp8 step as
+ *         w_scale_dev so that the step needs no host round trip.
+ *   status_out: one device int32 or NULL; 0, or SCE_DEV_SCALE_RANGE when W holds a
+ *         non-finite value (s_w is then 1 and the codes are unspecified).
+ *   workspace: at least SCE_REFRESH_WORKSPACE_BYTES of device memory, 256-byte aligned.
+ * Two kernels on `stream`; nothing is allocated and no host synchronisation happens.
+ */
+#define SCE_REFRESH_WORKSPACE_BYTES 8192
+SCE_API sce_status sce_refresh_e4m3_cache(const void* W, int64_t V, int64_t d, void* W8_out,
+                                          float* w_scale_out, int32_t* status_out,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sce_ce_rows -- the fused cross-entropy forward/backward of the step on its own, in
@@ -278,7 +357,7 @@ SCE_API sce_status sce_profile_collect(double* stage_ms, int nstages, int* ncall
 /* Human-readable name of an sce_status value (static string, never NULL). */
 SCE_API const char* sce_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 SCE_API int sce_abi_version(void);
 
 #ifdef __cplusplus

@@ -20,8 +20,9 @@ MAX_V_SAMPLED, MAX_V, MAX_D = 131072, 1048576, 16384
 STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
 
 EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sce_build_candidates_noalloc",
-           "sampled_ce_forward_backward",
-           "sampled_ce_forward_backward_fp8",
+           "sce_build_candidates_host",
+           "sampled_ce_forward_backward", "sampled_ce_forward_backward_prebuilt",
+           "sampled_ce_forward_backward_fp8", "sce_refresh_e4m3_cache",
            "sce_ce_rows_workspace_size", "sce_ce_rows", "sce_gather_rows",
            "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
 STAGES = ("candidates", "logits", "ce", "dx", "dx_reduce", "dw", "scatter")
@@ -50,15 +51,22 @@ def load_library(path: str = LIB_PATH):
     lib.sce_workspace_size.restype = i32
     lib.sce_build_candidates.argtypes = [p, p, i64, i64, i64, i64, i64, p, p, p, p, p, p, sz, p]
     lib.sce_build_candidates.restype = i32
+    lib.sce_build_candidates_host.argtypes = [p, p, i64, i64, i64, i64, i64, p, p, p, p]
+    lib.sce_build_candidates_host.restype = i32
     lib.sce_build_candidates_noalloc.argtypes = [p, p, i64, i64, i64, i64, i64, p, p, p, p, p, p]
     lib.sce_build_candidates_noalloc.restype = i32
     lib.sampled_ce_forward_backward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                                 p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.sampled_ce_forward_backward.restype = i32
-    lib.sampled_ce_forward_backward_fp8.argtypes = [p, p, ctypes.c_float, p, p, i64, i64, i64, i64,
-                                                    i64, i64, p, p, p, p, p, p, p, p, p, p, p,
-                                                    sz, p]
+    lib.sampled_ce_forward_backward_prebuilt.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64,
+                                                         i32, p, p, p, p, p, p, p, sz, p]
+    lib.sampled_ce_forward_backward_prebuilt.restype = i32
+    lib.sampled_ce_forward_backward_fp8.argtypes = [p, p, ctypes.c_float, p, p, p, i64, i64, i64,
+                                                    i64, i64, i64, p, p, p, p, p, p, p, p, p, p,
+                                                    p, sz, p]
     lib.sampled_ce_forward_backward_fp8.restype = i32
+    lib.sce_refresh_e4m3_cache.argtypes = [p, i64, i64, p, p, p, p, sz, p]
+    lib.sce_refresh_e4m3_cache.restype = i32
     lib.sce_ce_rows_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
     lib.sce_ce_rows_workspace_size.restype = i32
     lib.sce_ce_rows.argtypes = [p, i64, i64, i64, i32, p, p, p, p, p, p, p, sz, p]
@@ -118,17 +126,20 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def build_candidates(targets, prefix_targets, V, P, stride, offset, *, want_vocab_pos=False,
-                     ws=None):
+                     ws=None, outputs=None):
     """Device candidate build; returns dict of tensors (C, target_pos, prefix_pos,
-    vocab_pos or None, aux int64[4] = distinct, N, next_offset, device status)."""
+    vocab_pos or None, aux int64[4] = distinct, N, next_offset, device status).
+    `outputs` may pass a previous result to write into (same T, V, P)."""
     lib = load_library()
     dev = targets.device
     T = targets.shape[0]
-    C = torch.empty(P, dtype=torch.int32, device=dev)
-    tpos = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
-    ppos = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
-    vpos = torch.empty(V, dtype=torch.int32, device=dev) if want_vocab_pos else None
-    aux = torch.empty(4, dtype=torch.int64, device=dev)
+    o = outputs or {}
+    C = o["C"] if "C" in o else torch.empty(P, dtype=torch.int32, device=dev)
+    tpos = o["_tpos"] if "_tpos" in o else torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    ppos = o["_ppos"] if "_ppos" in o else torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    vpos = (o.get("vocab_pos") if o.get("vocab_pos") is not None
+            else torch.empty(V, dtype=torch.int32, device=dev)) if want_vocab_pos else None
+    aux = o["aux"] if "aux" in o else torch.empty(4, dtype=torch.int64, device=dev)
     nbytes = workspace_size(T, 8, V, P, SCE_F32)
     if ws is None:
         ws = workspace(nbytes, dev)
@@ -137,7 +148,42 @@ def build_candidates(targets, prefix_targets, V, P, stride, offset, *, want_voca
                                   _ptr(ws), ws.numel(), _stream(dev))
     if rc != 0:
         raise SceError("sce_build_candidates", rc)
-    return dict(C=C, target_pos=tpos[:T], prefix_pos=ppos[:T], vocab_pos=vpos, aux=aux)
+    return dict(C=C, target_pos=tpos[:T], prefix_pos=ppos[:T], vocab_pos=vpos, aux=aux,
+                _tpos=tpos, _ppos=ppos)
+
+
+def build_candidates_host(targets, prefix_targets, V, P, stride, offset, *, outputs=None):
+    """The candidate build on the host (sce_build_candidates_host). targets / prefix_targets:
+    int64 CPU tensors or numpy arrays (prefix may be None). Returns CPU tensors C, target_pos,
+    prefix_pos (or None) and aux (int64 [4]); `outputs` may pass tensors to write into
+    (pinned memory for an asynchronous upload). The call releases the interpreter lock while
+    it builds, so a Python thread can run it beside the GPU's work."""
+    import numpy as np
+
+    lib = load_library()
+    y = torch.as_tensor(np.ascontiguousarray(targets, dtype=np.int64)) if not torch.is_tensor(targets) else targets
+    p = None
+    if prefix_targets is not None:
+        p = (torch.as_tensor(np.ascontiguousarray(prefix_targets, dtype=np.int64))
+             if not torch.is_tensor(prefix_targets) else prefix_targets)
+    for t in (y, p):
+        if t is not None and (t.is_cuda or t.dtype != torch.int64 or not t.is_contiguous()):
+            raise ValueError("labels must be contiguous int64 host tensors")
+    T = y.shape[0]
+    o = dict(outputs or {})
+    if "C" not in o:
+        o["C"] = torch.empty(P, dtype=torch.int32)
+    if "target_pos" not in o:
+        o["target_pos"] = torch.empty(max(T, 1), dtype=torch.int32)
+    if "prefix_pos" not in o or (p is not None and o["prefix_pos"] is None):
+        o["prefix_pos"] = torch.empty(max(T, 1), dtype=torch.int32) if p is not None else None
+    if "aux" not in o:
+        o["aux"] = torch.empty(4, dtype=torch.int64)
+    rc = lib.sce_build_candidates_host(_ptr(y), _ptr(p), T, V, P, stride, offset, _ptr(o["C"]),
+                                       _ptr(o["target_pos"]), _ptr(o["prefix_pos"]), _ptr(o["aux"]))
+    if rc != 0:
+        raise SceError("sce_build_candidates_host", rc)
+    return o
 
 
 def build_candidates_noalloc(targets, prefix_targets, V, P, stride, offset, *,
@@ -220,11 +266,57 @@ def forward_backward(x, W, targets, prefix_targets, P, stride, offset, *, output
     return o
 
 
+def forward_backward_prebuilt(x, W, cand, *, outputs=None, ws=None, want_rows=False):
+    """The step from a candidate set built beforehand: `cand` is the dict that
+    build_candidates / build_candidates_noalloc returned (C, target_pos, prefix_pos or
+    None, aux). Returns the keys of forward_backward except C and the positions."""
+    lib = load_library()
+    dev = x.device
+    T, d = x.shape
+    V = W.shape[0]
+    P = cand["C"].shape[0]
+    if W.dtype != x.dtype or W.shape[1] != d:
+        raise ValueError("x and W must share dtype and hidden size")
+    for name, t in (("x", x), ("W", W)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for k in ("C", "target_pos", "prefix_pos"):
+        t = cand.get(k)
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{k} must be contiguous int32")
+    o = dict(outputs or {})
+    if "loss" not in o:
+        o["loss"] = torch.empty(1, dtype=torch.float32, device=dev)
+    if "dX" not in o:
+        o["dX"] = torch.empty_like(x)
+    if "dW" not in o:
+        o["dW"] = torch.empty_like(W)
+    if "aux" not in o:
+        o["aux"] = torch.empty(4, dtype=torch.int64, device=dev)
+    if want_rows:
+        for k in ("row_lse", "row_loss"):
+            if k not in o:
+                o[k] = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+    dt = dtype_code(x.dtype)
+    nbytes = workspace_size(T, d, V, P, dt)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    rc = lib.sampled_ce_forward_backward_prebuilt(
+        _ptr(x), _ptr(W), _ptr(cand["C"]), _ptr(cand["target_pos"]), _ptr(cand.get("prefix_pos")),
+        _ptr(cand.get("aux")), T, d, V, P, dt, _ptr(o["loss"]), _ptr(o["dX"]), _ptr(o["dW"]),
+        _ptr(o.get("row_lse")), _ptr(o.get("row_loss")), _ptr(o["aux"]), _ptr(ws), ws.numel(),
+        _stream(dev))
+    if rc != 0:
+        raise SceError("sampled_ce_forward_backward_prebuilt", rc)
+    return o
+
+
 def forward_backward_fp8(x, W8, w_scale, targets, prefix_targets, P, stride, offset, *,
                          outputs=None, ws=None, want_rows=False):
     """One sampled-CE step with e4m3 product operands. x [T,d] bf16, W8 [V,d] the lm_head
-    as e4m3 codes (torch.uint8 or torch.float8_e4m3fn), w_scale its float dequantisation
-    scale, labels as in forward_backward.
+    as e4m3 codes (torch.uint8 or torch.float8_e4m3fn), w_scale its dequantisation scale:
+    a Python float, or a one-element float32 device tensor that the step reads on the
+    device (refresh_e4m3_cache's "w_scale"), labels as in forward_backward.
 
     Returns the keys of forward_backward (dX and dW bf16) plus `scales` (fp32 [2]:
     s_x, s_g).
@@ -263,8 +355,14 @@ def forward_backward_fp8(x, W8, w_scale, targets, prefix_targets, P, stride, off
     nbytes = workspace_size(T, d, V, P, SCE_E4M3)
     if ws is None:
         ws = workspace(nbytes, dev)
+    if isinstance(w_scale, torch.Tensor):
+        if w_scale.dtype != torch.float32 or w_scale.device != dev or w_scale.numel() < 1:
+            raise ValueError("a device w_scale is a float32 tensor on x's device")
+        host_scale, dev_scale = 1.0, w_scale
+    else:
+        host_scale, dev_scale = float(w_scale), None
     rc = lib.sampled_ce_forward_backward_fp8(
-        _ptr(x), _ptr(W8), ctypes.c_float(w_scale), _ptr(targets), _ptr(prefix_targets), T, d, V,
+        _ptr(x), _ptr(W8), ctypes.c_float(host_scale), _ptr(dev_scale), _ptr(targets), _ptr(prefix_targets), T, d, V,
         P, stride, offset, _ptr(o["loss"]), _ptr(o["dX"]), _ptr(o["dW"]), _ptr(o["C"]),
         _ptr(o["target_pos"]), _ptr(o["prefix_pos"]), _ptr(o.get("row_lse")),
         _ptr(o.get("row_loss")), _ptr(o["aux"]), _ptr(o["scales"]), _ptr(ws), ws.numel(),
@@ -275,6 +373,35 @@ def forward_backward_fp8(x, W8, w_scale, targets, prefix_targets, P, stride, off
         o["C"] = o["C"][:P]
     o["target_pos"] = o["target_pos"][:T]
     o["prefix_pos"] = o["prefix_pos"][:T]
+    return o
+
+
+REFRESH_WORKSPACE_BYTES = 8192  # SCE_REFRESH_WORKSPACE_BYTES
+
+
+def refresh_e4m3_cache(W, *, outputs=None, ws=None):
+    """Rebuild the e4m3 lm_head cache on the device from W [V, d] bf16: returns dict
+    W8 (uint8 [V, d] codes), w_scale (float32 [1], s_w = max|W| / 448) and status
+    (int32 [1]: 0, or DEV_SCALE_RANGE for a non-finite W). `outputs` may pass a previous
+    result to overwrite (same shape)."""
+    lib = load_library()
+    dev = W.device
+    if W.dtype != torch.bfloat16 or W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous bf16 [V, d] tensor")
+    V, d = W.shape
+    o = dict(outputs or {})
+    if "W8" not in o:
+        o["W8"] = torch.empty(V, d, dtype=torch.uint8, device=dev)
+    if "w_scale" not in o:
+        o["w_scale"] = torch.empty(1, dtype=torch.float32, device=dev)
+    if "status" not in o:
+        o["status"] = torch.empty(1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(REFRESH_WORKSPACE_BYTES, dev)
+    rc = lib.sce_refresh_e4m3_cache(_ptr(W), V, d, _ptr(o["W8"]), _ptr(o["w_scale"]),
+                                    _ptr(o["status"]), _ptr(ws), ws.numel(), _stream(dev))
+    if rc != 0:
+        raise SceError("sce_refresh_e4m3_cache", rc)
     return o
 
 

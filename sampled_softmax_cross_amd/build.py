@@ -17,13 +17,15 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsampledce.so")
 SOURCES = ["api.hip", "candidates.hip", "gather_scatter.hip", "ce.hip", "gemm.hip", "gemm_bf16.hip",
-           "quant.hip"]
+           "quant.hip", "host_build.hip"]
 ARCH = os.environ.get("SCE_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # float division and square root correctly rounded (the e4m3 cache encodes W / s_w)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"),
 ]

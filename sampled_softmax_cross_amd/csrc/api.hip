@@ -235,7 +235,7 @@ using namespace sce;
 
 extern "C" {
 
-int sce_abi_version(void) { return 1; }
+int sce_abi_version(void) { return 2; }
 
 const char* sce_status_string(int status) {
   switch (status) {
@@ -298,58 +298,22 @@ sce_status sce_build_candidates_noalloc(const int64_t* targets, const int64_t* p
                                   static_cast<hipStream_t>(stream)));
 }
 
-sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64_t* targets,
-                                       const int64_t* prefix_targets, int64_t T, int64_t d,
-                                       int64_t V, int64_t P, int64_t stride, int64_t offset,
-                                       int dtype, float* loss, void* dX, void* dW,
-                                       int32_t* candidates_out, int32_t* target_pos_out,
-                                       int32_t* prefix_pos_out, float* row_lse_out,
-                                       float* row_loss_out, int64_t* aux_out, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
-  if (dtype == SCE_E4M3) return SCE_EINVAL;  // sampled_ce_forward_backward_fp8
-  sce_status st = check_sizes(T, d, V, P, dtype, true);
-  if (st != SCE_OK) return st;
-  if (W == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
-  if (T > 0 && (x == nullptr || targets == nullptr || dX == nullptr)) return SCE_EINVAL;
-  if ((x && !aligned16(x)) || !aligned16(W) || (dX && !aligned16(dX)) || !aligned16(dW))
-    return SCE_EINVAL;
-  int64_t s = 1;
-  if (P > 0) {
-    s = mod64(stride, V);
-    if (gcd64(s, V) != 1) return SCE_EINVAL;
-  }
-  const Plan p = make_plan(T, d, V, P, dtype, true);
-  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
-
-  const bool bf16 = dtype == SCE_BF16;
-  const size_t es = bf16 ? 2 : 4;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
-  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
-  int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
-  int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
-  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
-  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+// Everything of the bf16 / fp32 step after its candidate stage: logits, CE, dX, dW, the
+// scatter and the loss, on the workspace laid out by `p`.
+static hipError_t enqueue_products(const Plan& p, char* ws, const void* x, const void* W,
+                                   int64_t T, int64_t d, int64_t P, bool bf16, int32_t* counters,
+                                   const int32_t* cand, const int32_t* tpos, const int32_t* ppos,
+                                   float* row_loss, float* row_lse_out, float* loss, void* dX,
+                                   void* dW, int64_t* aux_out, StageMarks& marks, hipStream_t hs) {
   void* Z = ws + p.z;
   float* part = reinterpret_cast<float*>(ws + p.part);
   const void* WC = P > 0 ? static_cast<const void*>(ws + p.wc) : W;
   // dX's B operand: bf16 reads the transposed copy (r-major), f32 W_C itself (k-major)
   const void* dxB = bf16 ? static_cast<const void*>(ws + p.wt) : WC;
   const int64_t dxldb = bf16 ? p.ldt : p.ldwc;
-
-  StageMarks marks(hs);
-  marks.mark(SCE_STAGE_CANDIDATES);
-  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
-                                   tpos, ppos,
-                                   W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), dW,
-                                   (int)(d * es), hs, nullptr, -1, nullptr,
-                                   bf16 && T > 0 ? ws + p.wt : nullptr, p.ldt);
+  hipError_t e = hipSuccess;
   // bf16: dX reads W_C transposed; the gather wrote it when P > 0, W's own is made here
-  if (e == hipSuccess && bf16 && T > 0 && P == 0)
+  if (bf16 && T > 0 && P == 0)
     e = launch_transpose(WC, p.ldwc, (int)p.Peff, (int)d, 2, ws + p.wt, p.ldt, hs);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
@@ -388,10 +352,111 @@ sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64
                             (int)d, bf16, dW, &fin, hs);
   }
   marks.mark(SCE_NUM_STAGES);
+  return e;
+}
+
+// Host checks shared by the bf16 / fp32 step entry points.
+static sce_status check_step(const void* x, const void* W, const void* labels, int64_t T,
+                             int64_t d, int64_t V, int64_t P, int dtype, const float* loss,
+                             const void* dX, const void* dW) {
+  if (dtype == SCE_E4M3) return SCE_EINVAL;  // sampled_ce_forward_backward_fp8
+  const sce_status st = check_sizes(T, d, V, P, dtype, true);
+  if (st != SCE_OK) return st;
+  if (W == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
+  if (T > 0 && (x == nullptr || labels == nullptr || dX == nullptr)) return SCE_EINVAL;
+  if ((x && !aligned16(x)) || !aligned16(W) || (dX && !aligned16(dX)) || !aligned16(dW))
+    return SCE_EINVAL;
+  return SCE_OK;
+}
+
+sce_status sampled_ce_forward_backward(const void* x, const void* W, const int64_t* targets,
+                                       const int64_t* prefix_targets, int64_t T, int64_t d,
+                                       int64_t V, int64_t P, int64_t stride, int64_t offset,
+                                       int dtype, float* loss, void* dX, void* dW,
+                                       int32_t* candidates_out, int32_t* target_pos_out,
+                                       int32_t* prefix_pos_out, float* row_lse_out,
+                                       float* row_loss_out, int64_t* aux_out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  sce_status st = check_step(x, W, targets, T, d, V, P, dtype, loss, dX, dW);
+  if (st != SCE_OK) return st;
+  int64_t s = 1;
+  if (P > 0) {
+    s = mod64(stride, V);
+    if (gcd64(s, V) != 1) return SCE_EINVAL;
+  }
+  const Plan p = make_plan(T, d, V, P, dtype, true);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+
+  const bool bf16 = dtype == SCE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
+  int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
+  int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+
+  StageMarks marks(hs);
+  marks.mark(SCE_STAGE_CANDIDATES);
+  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
+                                   (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
+                                   tpos, ppos,
+                                   W, (int)(d * es), ws + p.wc, (int)(p.ldwc * es), dW,
+                                   (int)(d * es), hs, nullptr, -1, nullptr,
+                                   bf16 && T > 0 ? ws + p.wt : nullptr, p.ldt);
+  if (e == hipSuccess)
+    e = enqueue_products(p, ws, x, W, T, d, P, bf16, counters, cand, tpos, ppos, row_loss,
+                         row_lse_out, loss, dX, dW, aux_out, marks, hs);
+  return hip_status(e);
+}
+
+sce_status sampled_ce_forward_backward_prebuilt(const void* x, const void* W,
+                                                const int32_t* candidates,
+                                                const int32_t* target_pos,
+                                                const int32_t* prefix_pos,
+                                                const int64_t* build_aux, int64_t T, int64_t d,
+                                                int64_t V, int64_t P, int dtype, float* loss,
+                                                void* dX, void* dW, float* row_lse_out,
+                                                float* row_loss_out, int64_t* aux_out,
+                                                void* workspace, size_t workspace_bytes,
+                                                void* stream) {
+  sce_status st = check_step(x, W, target_pos, T, d, V, P, dtype, loss, dX, dW);
+  if (st != SCE_OK) return st;
+  if (P < 1 || candidates == nullptr) return SCE_EINVAL;  // a sampled candidate set only
+  const Plan p = make_plan(T, d, V, P, dtype, true);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+
+  const bool bf16 = dtype == SCE_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* cand = reinterpret_cast<int32_t*>(ws + p.cand);
+  int32_t* tpos = reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+
+  StageMarks marks(hs);
+  marks.mark(SCE_STAGE_CANDIDATES);
+  hipError_t e = launch_candidates_prebuilt(candidates, target_pos, prefix_pos, build_aux, (int)T,
+                                            (int)V, (int)P, counters, cand, bits, tpos, ppos, W,
+                                            (int)(d * es), ws + p.wc, (int)(p.ldwc * es), dW,
+                                            (int)(d * es), bf16 && T > 0 ? ws + p.wt : nullptr,
+                                            p.ldt, hs);
+  if (e == hipSuccess)
+    e = enqueue_products(p, ws, x, W, T, d, P, bf16, counters, cand, tpos, ppos, row_loss,
+                         row_lse_out, loss, dX, dW, aux_out, marks, hs);
   return hip_status(e);
 }
 
 sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float w_scale,
+                                           const float* w_scale_dev,
                                            const int64_t* targets, const int64_t* prefix_targets,
                                            int64_t T, int64_t d, int64_t V, int64_t P,
                                            int64_t stride, int64_t offset, float* loss, void* dX,
@@ -402,7 +467,10 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
                                            size_t workspace_bytes, void* stream) {
   sce_status st = check_sizes(T, d, V, P, SCE_E4M3, true);
   if (st != SCE_OK) return st;
-  if (!(w_scale > 0.f) || w_scale > 3.0e38f) return SCE_EINVAL;  // also rejects NaN
+  if (w_scale_dev == nullptr && (!(w_scale > 0.f) || w_scale > 3.0e38f))
+    return SCE_EINVAL;  // also rejects NaN; a device scale is checked on the device
+  if (w_scale_dev != nullptr && (reinterpret_cast<uintptr_t>(w_scale_dev) & 3) != 0)
+    return SCE_EINVAL;
   if (W8 == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
   if (T > 0 && (x == nullptr || targets == nullptr || dX == nullptr)) return SCE_EINVAL;
   if ((x && !aligned16(x)) || !aligned16(W8) || (dX && !aligned16(dX)) || !aligned16(dW))
@@ -441,7 +509,8 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
                                    W8, (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2), hs,
                                    x, T * d, &amax_parts);
   if (e == hipSuccess)
-    e = launch_quant_x(x, T * d, counters, w_scale, x8, scales, scales_out, hs, amax_parts);
+    e = launch_quant_x(x, T * d, counters, w_scale, w_scale_dev, x8, scales, scales_out, hs,
+                       amax_parts);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
     GemmArgs g{x8, d, WC, p.ldwc, Z, p.ldz, T, p.Peff, d, 1, 0, scales + kScaleLogits};
@@ -482,6 +551,24 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   }
   marks.mark(SCE_NUM_STAGES);
   return hip_status(e);
+}
+
+sce_status sce_refresh_e4m3_cache(const void* W, int64_t V, int64_t d, void* W8_out,
+                                  float* w_scale_out, int32_t* status_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  static_assert(kCounterWords * sizeof(int32_t) <= SCE_REFRESH_WORKSPACE_BYTES,
+                "the refresh's partial maxima fit its workspace");
+  if (V < 1 || V > SCE_MAX_V || d < 16 || d > SCE_MAX_D || d % 16 != 0) return SCE_EINVAL;
+  if (W == nullptr || W8_out == nullptr || w_scale_out == nullptr) return SCE_EINVAL;
+  if (!aligned16(W) || !aligned16(W8_out) || (reinterpret_cast<uintptr_t>(w_scale_out) & 3) ||
+      (reinterpret_cast<uintptr_t>(status_out) & 3))
+    return SCE_EINVAL;
+  if (workspace == nullptr || workspace_bytes < SCE_REFRESH_WORKSPACE_BYTES ||
+      (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return SCE_EWORKSPACE;
+  return hip_status(launch_refresh_e4m3(W, V * d, W8_out, w_scale_out, status_out,
+                                        static_cast<int32_t*>(workspace),
+                                        static_cast<hipStream_t>(stream)));
 }
 
 // ---- building blocks on their own ---------------------------------------------

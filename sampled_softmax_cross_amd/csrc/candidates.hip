@@ -243,7 +243,8 @@ __global__ __launch_bounds__(256) void k_remap_gather(
     int32_t* __restrict__ counters, int remap_blocks, const uint4* __restrict__ W,
     const int32_t* __restrict__ C, int row_vecs, uint4* __restrict__ WC, int wc_vecs,
     int gather_blocks, uint4* __restrict__ dW, int dw_vecs, int zero_blocks,
-    int32_t* __restrict__ vocab_pos, uint16_t* __restrict__ WT, int64_t ldt, int tr_x) {
+    int32_t* __restrict__ vocab_pos, uint16_t* __restrict__ WT, int64_t ldt, int tr_x,
+    const int32_t* __restrict__ tpos_in, const int32_t* __restrict__ ppos_in) {
   const int b = (int)blockIdx.x;
   if (b >= remap_blocks + gather_blocks + zero_blocks) {
     const int c = (b - remap_blocks - gather_blocks - zero_blocks) * 256 + (int)threadIdx.x;
@@ -267,7 +268,19 @@ __global__ __launch_bounds__(256) void k_remap_gather(
   __shared__ int scratch[256 / kWave + 1];
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   int n = 0;
-  if (t < T) {
+  if (t < T && tpos_in != nullptr) {
+    // Positions given (a candidate set built beforehand): copied, with a position outside
+    // [-1, P) flagged and replaced by -1.
+    int tp = tpos_in[t];
+    int pp = ppos_in != nullptr ? ppos_in[t] : -1;
+    const bool bad = tp < -1 || tp >= P || pp < -1 || pp >= P;
+    if (tp < -1 || tp >= P) tp = -1;
+    if (pp < -1 || pp >= P) pp = -1;
+    if (bad) atomicOr(&counters[kStatus], kDevLabelRange);
+    target_pos[t] = tp;
+    prefix_pos[t] = pp;
+    n += (tp >= 0) + (pp >= 0);
+  } else if (t < T) {
     // Both labels, then (sampled) their bitmap words, each set of loads issued before
     // any of them is used; a label outside [0, V) looks up class 0 and is dropped.
     const int64_t y = targets[t];
@@ -286,6 +299,40 @@ __global__ __launch_bounds__(256) void k_remap_gather(
   }
   const int s = block_sum_int(n, scratch);
   if (threadIdx.x == 0 && s) atomicAdd(&counters[kNumLabels], s);
+}
+
+// A candidate set built beforehand (P > 0): one workgroup clears the step's counters,
+// copies C to the step's own array with every class that is outside [0, V) or not above
+// its predecessor flagged (SCE_DEV_LABEL_RANGE) and replaced by class 0 (so every later
+// access stays in bounds), leaves the candidate bitmap for the launch that clears dW's
+// other rows, and takes the distinct count, next offset and device bits from the build's
+// aux when given (else -1, -1, 0).
+__global__ __launch_bounds__(kBuildThreads) void k_cand_prebuilt(
+    const int32_t* __restrict__ C_in, int V, int P, const int64_t* __restrict__ build_aux,
+    int32_t* __restrict__ counters, int32_t* __restrict__ C, uint32_t* __restrict__ bits) {
+  extern __shared__ uint32_t mark[];
+  __shared__ int scratch[kBuildThreads / kWave + 1];
+  const int W = (V + 31) >> 5;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid < kNumCounters) counters[tid] = 0;
+  for (int w = tid; w < W; w += nt) mark[w] = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int i = tid; i < P; i += nt) {
+    const int c = C_in[i];
+    const int prev = i > 0 ? C_in[i - 1] : -1;
+    const bool ok = c >= 0 && c < V && c > prev;
+    bad |= !ok;
+    C[i] = ok ? c : 0;
+    if (ok) atomicOr(&mark[c >> 5], 1u << (c & 31));
+  }
+  const int any_bad = block_sum_int(bad, scratch);  // (contains barriers)
+  for (int w = tid; w < W; w += nt) bits[w] = mark[w];
+  if (tid == 0) {
+    counters[kStatus] = (any_bad ? kDevLabelRange : 0) | (build_aux ? (int)build_aux[3] : 0);
+    counters[kDistinct] = build_aux ? (int)build_aux[0] : -1;
+    counters[kNextOffset] = build_aux ? (int)build_aux[2] : -1;
+  }
 }
 
 __global__ void k_write_aux(const int32_t* __restrict__ counters, int64_t* __restrict__ aux) {
@@ -328,7 +375,37 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                        reinterpret_cast<const uint4*>(W), C, row_bytes / 16,
                        reinterpret_cast<uint4*>(WC), wc_row_bytes / 16, gather_blocks,
                        reinterpret_cast<uint4*>(dW), dw_row_bytes / 16, zero_blocks, vocab_pos,
-                       static_cast<uint16_t*>(tr ? WT : nullptr), ldt, tr_x);
+                       static_cast<uint16_t*>(tr ? WT : nullptr), ldt, tr_x, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_candidates_prebuilt(const int32_t* C_in, const int32_t* tpos_in,
+                                      const int32_t* ppos_in, const int64_t* build_aux, int T,
+                                      int V, int P, int32_t* counters, int32_t* C, uint32_t* bits,
+                                      int32_t* target_pos, int32_t* prefix_pos, const void* W,
+                                      int row_bytes, void* WC, int wc_row_bytes, void* dW,
+                                      int dw_row_bytes, void* WT, int64_t ldt, hipStream_t s) {
+  if (P < 1 || V > kMaxBitmapClasses) return hipErrorInvalidValue;
+  const size_t lds = (size_t)((V + 31) / 32) * sizeof(uint32_t);
+  hipLaunchKernelGGL(k_cand_prebuilt, dim3(1), dim3(kBuildThreads), lds, s, C_in, V, P, build_aux,
+                     counters, C, bits);
+  // the remap launch in its positions mode: the same gather (with the transpose), zero rows
+  // and label counting as after a build, with the positions copied instead of derived
+  const int remap_blocks = (T + 255) / 256;
+  const bool tr = WT != nullptr && W != nullptr;
+  const int tr_x = tr ? (int)((ldt + kTrTile - 1) / kTrTile) : 1;
+  const int gather_blocks = tr ? tr_x * ((row_bytes / 2 + kTrTile - 1) / kTrTile)
+                               : (W != nullptr ? gather_block_count(P, row_bytes / 16) : 0);
+  const int zero_blocks = dW != nullptr ? zero_block_count(V, dw_row_bytes / 16) : 0;
+  const int grid = remap_blocks + gather_blocks + zero_blocks;
+  if (grid > 0)
+    hipLaunchKernelGGL(k_remap_gather, dim3(grid), dim3(256), 0, s, nullptr, nullptr, T, V, P,
+                       bits, nullptr, target_pos, prefix_pos, counters, remap_blocks,
+                       reinterpret_cast<const uint4*>(W), C, row_bytes / 16,
+                       reinterpret_cast<uint4*>(WC), wc_row_bytes / 16, gather_blocks,
+                       reinterpret_cast<uint4*>(dW), dw_row_bytes / 16, zero_blocks, nullptr,
+                       static_cast<uint16_t*>(tr ? WT : nullptr), ldt, tr_x, tpos_in,
+                       T > 0 ? ppos_in : nullptr);
   return hipGetLastError();
 }
 

@@ -27,6 +27,17 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                              const void* amax_x = nullptr, int64_t amax_n = -1,
                              int* amax_parts = nullptr, void* WT = nullptr, int64_t ldt = 0);
 hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s);
+// The candidate stage for a set built beforehand (P > 0, V <= kMaxBitmapClasses): C_in
+// [P] ascending classes and the label positions tpos_in / ppos_in (ppos_in may be null)
+// are checked and copied to C / target_pos / prefix_pos, the counters set (distinct count,
+// next offset and device bits from build_aux when given), then the same gather, transpose
+// and zero rows as launch_candidates.
+hipError_t launch_candidates_prebuilt(const int32_t* C_in, const int32_t* tpos_in,
+                                      const int32_t* ppos_in, const int64_t* build_aux, int T,
+                                      int V, int P, int32_t* counters, int32_t* C, uint32_t* bits,
+                                      int32_t* target_pos, int32_t* prefix_pos, const void* W,
+                                      int row_bytes, void* WC, int wc_row_bytes, void* dW,
+                                      int dw_row_bytes, void* WT, int64_t ldt, hipStream_t s);
 
 // Row gather, one block of 256 lanes per kGatherRows rows: 32 lanes per row, each
 // moving whole 16-byte vectors, every load of a lane issued before its stores. Rows of
@@ -179,12 +190,19 @@ hipError_t launch_ce_rows_g8(const void* Z, int64_t ldz, int T, int P, const int
                              float* row_lse, const G8Out& go, hipStream_t s);
 
 // e4m3 step: s_x from max|x| over bf16 x [n] (n a multiple of 8), and x8 = e4m3(x / s_x)
-// (bytes, same layout); fills the scale table's x entries (w_scale, s_x) and
-// scales_out[0] when given. max|x| comes from the amax_parts partials that
+// (bytes, same layout); fills the scale table's x entries (the cache's scale: *w_scale_dev
+// when given, else w_scale; and s_x) and scales_out[0] when given. max|x| comes from the amax_parts partials that
 // launch_candidates left in counters[kAmaxX ...] (amax_parts > 0), else from an amax
 // launch of its own.
-hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_scale, void* x8,
-                          float* scales, float* scales_out, hipStream_t s, int amax_parts = 0);
+hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_scale,
+                          const float* w_scale_dev, void* x8, float* scales, float* scales_out,
+                          hipStream_t s, int amax_parts = 0);
+// The e4m3 lm_head cache refresh: W8 = e4m3(W / s_w), s_w = max|W| / 448 (float32; 1 for an
+// all-zero W) written to *scale_out, over n bf16 values (a multiple of 8). part: kCounterWords
+// ints of scratch for the per-workgroup maxima; status (may be null) is set to 0, or to
+// kDevScaleRange when W holds a non-finite value.
+hipError_t launch_refresh_e4m3(const void* W, int64_t n, void* W8, float* scale_out,
+                               int32_t* status, int32_t* part, hipStream_t s);
 
 // max|x| partial of one amax block (kBuildThreads lanes; block `b` of `nb`) over nvec
 // 16-byte bf16 vectors, written as the magnitude's bits to counters[kAmaxX + b].

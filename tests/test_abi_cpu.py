@@ -41,7 +41,7 @@ def test_binding_constants_match_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.sce_abi_version() == 1
+    assert lib.sce_abi_version() == 2
     for code in range(4):
         assert lib.sce_status_string(code).decode().startswith("SCE_")
     assert lib.sce_status_string(99) == b"unknown sce_status"
@@ -134,7 +134,7 @@ def test_fp8_host_checks(lib):
     assert lib.sce_workspace_size(16, 24, 100, 10, binding.SCE_E4M3, ctypes.byref(out)) == 1  # d % 16
     f = lib.sampled_ce_forward_backward_fp8
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
-    args = dict(x=fake, W8=fake, ws=ctypes.c_float(0.01), y=fake, p=None, T=4, d=16, V=16, P=4,
+    args = dict(x=fake, W8=fake, ws=ctypes.c_float(0.01), wsd=None, y=fake, p=None, T=4, d=16, V=16, P=4,
                 stride=3, off=0, loss=fake, dX=fake, dW=fake, c=None, tp=None, pp=None, lse=None,
                 rl=None, aux=None, sc=None, wsp=None, wsb=0, s=None)
 
@@ -151,10 +151,36 @@ def test_fp8_host_checks(lib):
     assert call(W8=None) == 1
     assert call(x=ctypes.c_void_p((1 << 20) + 8)) == 1   # misaligned
     assert call(wsp=fake, wsb=16) == 2                   # too small
+    # a device scale replaces the host one (checked on the device), so a bad host value
+    # with a device scale passes the host checks (and stops at the workspace)
+    assert call(ws=ctypes.c_float(0.0), wsd=fake) == 2
+    assert call(ws=ctypes.c_float(0.0), wsd=ctypes.c_void_p((1 << 20) + 2)) == 1  # misaligned
     g = lib.sampled_ce_forward_backward
     assert g(fake, fake, fake, None, 4, 16, 16, 4, 3, 0, binding.SCE_E4M3, fake, fake, fake, None, None,
              None, None, None, None, None, 0, None) == 1  # the e4m3 step has its own entry point
 
+
+
+def test_refresh_host_checks(lib):
+    r = lib.sce_refresh_e4m3_cache
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    nb = binding.REFRESH_WORKSPACE_BYTES
+    args = dict(W=fake, V=16, d=16, W8=fake, sc=fake, st=None, wsp=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return r(*a.values())
+
+    assert call() == 2                                    # no workspace
+    assert call(wsp=fake, wsb=nb - 1) == 2                # too small
+    assert call(wsp=ctypes.c_void_p((1 << 20) + 64), wsb=nb) == 2  # misaligned workspace
+    assert call(d=8, wsp=fake, wsb=nb) == 1               # d % 16 != 0
+    assert call(V=0, wsp=fake, wsb=nb) == 1
+    assert call(V=binding.MAX_V + 1, wsp=fake, wsb=nb) == 1
+    assert call(W=None, wsp=fake, wsb=nb) == 1
+    assert call(sc=None, wsp=fake, wsb=nb) == 1
+    assert call(W8=ctypes.c_void_p((1 << 20) + 8), wsp=fake, wsb=nb) == 1
+    assert call(st=ctypes.c_void_p((1 << 20) + 2), wsp=fake, wsb=nb) == 1
 
 
 def test_noalloc_build_host_checks(lib):

@@ -30,7 +30,7 @@ CASES = [
 
 
 def _w8(W):
-    codes, scale = synth.e4m3_cache(W)
+    codes, scale = fp8.e4m3_cache(synth.to_f64(W, "bf16"))
     return codes, scale, torch.from_numpy(codes).cuda()
 
 

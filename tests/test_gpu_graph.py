@@ -5,6 +5,7 @@ other eager work on the device in between, must reproduce the eager call bit for
 import pytest
 import torch
 
+from oracle import fp8
 from sampled_softmax_cross_amd import binding, synth
 from tests.gpu_util import labels_dev, to_dev
 
@@ -14,8 +15,8 @@ KEYS = ("loss", "dX", "dW", "C", "target_pos", "prefix_pos", "aux", "row_lse", "
 
 
 def _inputs(dtype, T=300, d=64, V=1000, P=333):
-    x, W, y, p = synth.small_case(11, T, d, V, "bf16" if dtype == "e4m3" else dtype, prefix=True,
-                                  ignore_frac=0.05)
+    x, W, y, p = synth.small_case(11, T, d, V, "bf16" if dtype.startswith("e4m3") else dtype,
+                                  prefix=True, ignore_frac=0.05)
     return x, W, y, p, P
 
 
@@ -23,16 +24,30 @@ def _call(fn, outs, ws):
     return fn(outputs=outs, ws=ws, want_rows=True)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "e4m3"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "e4m3", "e4m3_refresh"])
 def test_captured_step_replays_bitwise(dtype):
+    """e4m3_refresh: the cache refresh from bf16 W and the e4m3 step reading its scale on
+    the device, captured together."""
     print(f"graph capture {dtype}", flush=True)
     x, W, y, p, P = _inputs(dtype)
     T, d = x.shape
     V = W.shape[0]
-    xd = to_dev(x, "bf16" if dtype == "e4m3" else dtype)
+    xd = to_dev(x, "bf16" if dtype.startswith("e4m3") else dtype)
     yd, pd = labels_dev(y), labels_dev(p)
-    if dtype == "e4m3":
-        codes, scale = synth.e4m3_cache(W)
+    if dtype == "e4m3_refresh":
+        Wd = to_dev(W, "bf16")
+        cache = dict(W8=torch.empty(V, d, dtype=torch.uint8, device=xd.device),
+                     w_scale=torch.empty(1, dtype=torch.float32, device=xd.device),
+                     status=torch.empty(1, dtype=torch.int32, device=xd.device))
+        rws = torch.empty(binding.REFRESH_WORKSPACE_BYTES, dtype=torch.uint8, device=xd.device)
+
+        def fn(**kw):
+            binding.refresh_e4m3_cache(Wd, outputs=cache, ws=rws)
+            return binding.forward_backward_fp8(xd, cache["W8"], cache["w_scale"], yd, pd, P, 7, 3,
+                                                **kw)
+        nbytes = binding.workspace_size(T, d, V, P, binding.SCE_E4M3)
+    elif dtype == "e4m3":
+        codes, scale = fp8.e4m3_cache(synth.to_f64(W, "bf16"))
         W8 = torch.from_numpy(codes).cuda()
         fn = lambda **kw: binding.forward_backward_fp8(xd, W8, scale, yd, pd, P, 7, 3, **kw)
         nbytes = binding.workspace_size(T, d, V, P, binding.SCE_E4M3)
