@@ -38,6 +38,8 @@ struct Plan {
   int64_t ldt = 0;    // bf16: row pitch of W_C's transpose [d, P_eff] (elements)
   int64_t ldg = 0;    // e4m3 step: row pitch of the e4m3 gradient (bytes)
   int splits = 1;     // k-split of the dW product (fp32 partials reduced by the scatter)
+  int dw_whole = 0;   // dW tiles stored whole into dW (rows [0, dw_r0) of the candidate order)
+  int64_t dw_r0 = 0;  // first row of the k-split dW tiles (their partials hold rows dw_r0..)
   int dx_splits = 1;  // k-split of the dX product (fp32 partials reduced into dX)
   size_t counters = 0, bits = 0, wpre = 0, cand = 0, tpos = 0, ppos = 0, row_loss = 0;
   size_t wc = 0, wt = 0, z = 0, part = 0, total = 0;
@@ -85,17 +87,23 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
       p.x8 = take((size_t)T * d);
       p.g8 = take((size_t)T * p.ldg);
       p.scales = take(kNumScales * sizeof(float));
-      p.splits = gemm_fp8_dw_splits(p.Peff, d, T);
+      const DwPlan dw = gemm_fp8_dw_plan(p.Peff, d, T);
+      p.splits = dw.splits;
+      p.dw_whole = dw.whole;
+      p.dw_r0 = dw.r0;
       p.dx_splits = gemm_fp8_dx_splits(T, d, p.Peff);
     } else if (dtype == SCE_BF16) {
-      p.splits = gemm_bf16_dw_splits(p.Peff, d, T);
+      const DwPlan dw = gemm_bf16_dw_plan(p.Peff, d, T);
+      p.splits = dw.splits;
+      p.dw_whole = dw.whole;
+      p.dw_r0 = dw.r0;
       p.dx_splits = gemm_bf16_dx_splits(T, d, p.Peff);
     } else {
       p.splits = gemm_f32_splits(p.Peff, d, T);
       p.dx_splits = gemm_f32_splits(T, d, p.Peff);
     }
     // One region serves both products' partials (dX's are reduced before dW runs).
-    const size_t dw_part = (size_t)p.splits * p.Peff * d;
+    const size_t dw_part = (size_t)p.splits * (p.Peff - p.dw_r0) * d;
     const size_t dx_part = p.dx_splits > 1 ? (size_t)p.dx_splits * T * d : 0;
     p.part = take((dw_part > dx_part ? dw_part : dx_part) * sizeof(float));
   }
@@ -340,16 +348,21 @@ static hipError_t enqueue_products(const Plan& p, char* ws, const void* x, const
                             hs);
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess) {
-    GemmArgs g{Z, p.ldz, x, d, part, d, p.Peff, d, T, p.splits, p.Peff * d};
+    GemmArgs g{Z, p.ldz, x, d, part, d, p.Peff, d, T, p.splits, (p.Peff - p.dw_r0) * d};
+    g.dw = DwOut{dW, d, P > 0 ? cand : nullptr, p.dw_whole, p.dw_r0};
     e = launch_gemm(Gemm::DW, bf16, g, hs);
   }
   marks.mark(SCE_STAGE_SCATTER);
   if (e == hipSuccess) {
-    // The candidate rows of dW (the others were cleared by the remap launch); the
-    // launch's extra block also finishes the loss.
+    // The k-split candidate rows of dW, r0.. (the whole tiles' rows were stored by the
+    // product; the rows outside C were cleared by the remap launch); the launch's extra
+    // block also finishes the loss.
     const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
-    e = launch_scatter_rows(part, p.splits, p.Peff * d, P > 0 ? cand : nullptr, (int)p.Peff,
-                            (int)d, bf16, dW, &fin, hs);
+    const int64_t r0 = p.dw_r0;
+    e = launch_scatter_rows(part, p.splits, (p.Peff - r0) * d, P > 0 ? cand + r0 : nullptr,
+                            (int)(p.Peff - r0), (int)d, bf16,
+                            P > 0 ? dW : static_cast<char*>(dW) + r0 * d * (bf16 ? 2 : 4), &fin,
+                            hs);
   }
   marks.mark(SCE_NUM_STAGES);
   return e;
@@ -538,16 +551,21 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
                             hs);
   marks.mark(SCE_STAGE_DW);
   if (e == hipSuccess && T > 0) {
-    GemmArgs g{g8, p.ldg, x8, d, part, d, p.Peff, d, T, p.splits, p.Peff * d, scales + kScaleDw};
+    GemmArgs g{g8, p.ldg, x8, d, part, d, p.Peff, d, T, p.splits, (p.Peff - p.dw_r0) * d,
+               scales + kScaleDw};
+    g.dw = DwOut{dW, d, P > 0 ? cand : nullptr, p.dw_whole, p.dw_r0};
     e = launch_gemm_fp8(Gemm::DW, g, hs);
   }
   marks.mark(SCE_STAGE_SCATTER);
   if (e == hipSuccess) {
     const LossOut fin{row_loss, (int)T, counters, loss, aux_out};
-    // T = 0: no product ran; the candidate rows are written as zeros (a sum over no
-    // partials), the others were cleared by the remap launch.
-    e = launch_scatter_rows(part, T > 0 ? p.splits : 0, p.Peff * d, P > 0 ? cand : nullptr,
-                            (int)p.Peff, (int)d, true, dW, &fin, hs);
+    // T = 0: no product ran; every candidate row is written as zeros (a sum over no
+    // partials), the others were cleared by the remap launch. Otherwise the k-split rows
+    // r0.. (the product stored the whole tiles' rows).
+    const int64_t r0 = T > 0 ? p.dw_r0 : 0;
+    e = launch_scatter_rows(part, T > 0 ? p.splits : 0, (p.Peff - r0) * d,
+                            P > 0 ? cand + r0 : nullptr, (int)(p.Peff - r0), (int)d, true,
+                            P > 0 ? dW : static_cast<char*>(dW) + r0 * d * 2, &fin, hs);
   }
   marks.mark(SCE_NUM_STAGES);
   return hip_status(e);

@@ -245,7 +245,7 @@ template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int N
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
     const void* __restrict__ A, int64_t lda, const void* __restrict__ B, int64_t ldb,
     void* __restrict__ Cout, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t kps,
-    int64_t split_stride, int splits, const float* __restrict__ scale) {
+    int64_t split_stride, int splits, const float* __restrict__ scale, DwOut dwo) {
   using frag_t = typename MfmaElem<EB>::frag_t;
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -280,24 +280,54 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
   const int wm = wid / WGN, wn = wid % WGN;
   const int nbx = (int)((N + BN - 1) / BN), nby = (int)((M + BM - 1) / BM);
   const int ntiles = nbx * nby;
-  const int nunits = ntiles * splits;
+  // kOutDW: dwo.whole whole units, then the other tiles' k-split units
+  const int whole = OUT == kOutDW ? dwo.whole : 0;
+  const int nunits = whole + (ntiles - whole) * splits;
   const int G = gridDim.x;
   if ((int)blockIdx.x >= nunits) return;
   const int my_units = (nunits - 1 - (int)blockIdx.x) / G + 1;
-  const int nk = (int)(kps / SK);  // stages per unit (kps is a positive multiple)
+  const int nk_split = (int)(kps / SK);                  // stages of a split unit
+  const int nk_whole = (int)((K + SK - 1) / SK);         // stages of a whole unit
 
   struct Unit {
     int64_t m0, n0, kb, ke;
+    int nk;     // stages
+    int split;  // k-range index; -1: a whole unit (kOutDW)
   };
   const int gm = group_rows(nbx, (int64_t)BM * BN * (OUT == kOutBF16 ? 2 : 4));
   auto unit = [&](int i) {
+    const int u = (int)blockIdx.x + i * G;
     int tm, tn, sp;
-    unit_of((int)blockIdx.x + i * G, nby, nbx, splits, gm, tm, tn, sp);
     Unit c;
+    if constexpr (OUT == kOutDW) {
+      // XCD-contiguous renumbering within each kind; tiles row-major (nbx <= 4)
+      int t;
+      if (u < whole) {
+        t = xcd_order(u, whole);
+        sp = -1;
+      } else {
+        const int rem = ntiles - whole;
+        const int lid = xcd_order(u - whole, rem * splits);
+        sp = lid / rem;
+        t = whole + (lid - sp * rem);
+      }
+      tm = t / nbx;
+      tn = t - tm * nbx;
+    } else {
+      unit_of(u, nby, nbx, splits, gm, tm, tn, sp);
+    }
     c.m0 = (int64_t)tm * BM;
     c.n0 = (int64_t)tn * BN;
-    c.kb = (int64_t)sp * kps;
-    c.ke = K < c.kb + kps ? K : c.kb + kps;
+    c.split = sp;
+    if (sp < 0) {
+      c.kb = 0;
+      c.ke = K;
+      c.nk = nk_whole;
+    } else {
+      c.kb = (int64_t)sp * kps;
+      c.ke = K < c.kb + kps ? K : c.kb + kps;
+      c.nk = nk_split;
+    }
     return c;
   };
 
@@ -321,7 +351,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
   Cursor ca{0, 0, unit(0)};
   Cursor cb = ca;  // B's cursor when NSB < NS
   auto advance = [&](Cursor& q) {
-    if (++q.is == nk) {
+    if (++q.is == q.c.nk) {
       q.is = 0;
       ++q.iu;
       if (q.iu < my_units) q.c = unit(q.iu);
@@ -416,7 +446,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    for (int s = 0; s < nk; ++s, ++g) {
+    for (int s = 0; s < cc.nk; ++s, ++g) {
 #pragma unroll
       for (int q = 0; q + 1 < KS; ++q) {
         // k-step q of stage g, with the reads of its k-step q + 1 in its shadow.
@@ -450,12 +480,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] *= sc;
     }
-    if constexpr (kStaged)
+    if constexpr (kStaged) {
       store_acc_bf16_lds<TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow, cc.n0 + bcol, lane,
                                  lds + kRing + wid * 256);
-    else
+    } else if constexpr (OUT == kOutDW) {
+      if (cc.split < 0)
+        store_acc_rows_bf16<TM, TN>(acc, dwo.dW, dwo.ldw, dwo.rowmap, M, N, cc.m0 + arow + l32,
+                                    cc.n0 + bcol, lane >> 5);
+      else
+        store_acc<kOutF32Split, TM, TN>(acc, Cout, ldc, M - dwo.r0, N,
+                                        cc.m0 - dwo.r0 + arow + l32, cc.n0 + bcol, lane >> 5,
+                                        cc.split * split_stride);
+    } else {
       store_acc<OUT, TM, TN>(acc, Cout, ldc, M, N, cc.m0 + arow + l32, cc.n0 + bcol, lane >> 5,
                              OUT == kOutF32Split ? (cc.kb / kps) * split_stride : 0);
+    }
   }
   // The ring's last loads (of stages past the last unit: zeros) land before the
   // workgroup's LDS is released.
@@ -465,19 +504,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
 #define SCE_GEMM_INST(BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL, EB)                 \
   template __global__ void k_gemm_mfma<BM, BN, WGM, WGN, AK, BK, OUT, NS, OCC, SK, NSB, IL, EB>( \
       const void*, int64_t, const void*, int64_t, void*, int64_t, int64_t, int64_t, int64_t,     \
-      int64_t, int64_t, int, const float*);
+      int64_t, int64_t, int, const float*, DwOut);
 SCE_GEMM_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 64, 2, true, 2)
 SCE_GEMM_INST(256, 192, 4, 2, false, false, kOutBF16, 2, 1, 64, 2, true, 2)
 SCE_GEMM_INST(256, 192, 4, 2, false, false, kOutF32Split, 2, 1, 64, 2, true, 2)
 SCE_GEMM_INST(128, 256, 2, 4, false, false, kOutBF16, 3, 2, 32, 3, true, 2)
 SCE_GEMM_INST(128, 256, 2, 4, false, false, kOutF32Split, 3, 2, 32, 3, true, 2)
 SCE_GEMM_INST(256, 256, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false, 2)
+SCE_GEMM_INST(256, 256, 4, 2, true, true, kOutDW, 2, 1, 64, 2, false, 2)
 SCE_GEMM_INST(256, 256, 2, 4, false, false, kOutBF16, 2, 1, 128, 2, true, 1)
 SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutBF16, 2, 1, 128, 2, false, 1)
 SCE_GEMM_INST(256, 192, 4, 2, false, true, kOutF32Split, 2, 1, 128, 2, false, 1)
 SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutBF16, 2, 1, 128, 2, true, 1)
 SCE_GEMM_INST(128, 256, 2, 4, false, true, kOutF32Split, 2, 1, 128, 2, true, 1)
 SCE_GEMM_INST(256, 256, 4, 2, true, true, kOutF32Split, 2, 1, 128, 2, false, 1)
+SCE_GEMM_INST(256, 256, 4, 2, true, true, kOutDW, 2, 1, 128, 2, false, 1)
 #undef SCE_GEMM_INST
 
 template <int BM, int BN, int WGM, int WGN, bool A_KM, bool B_KM, int OUT, int NS, int OCC,
@@ -489,7 +530,12 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   if (kps == 0) kps = SK;
   const int64_t gx = (a.N + BN - 1) / BN, gy = (a.M + BM - 1) / BM;
   if (gx == 0 || gy == 0) return hipGetLastError();
-  const int64_t units = gx * gy * splits;
+  const int64_t whole = OUT == kOutDW ? a.dw.whole : 0;
+  if (OUT == kOutDW &&
+      (gx > 4 || whole < 0 || whole > gx * gy || whole % gx != 0 || a.dw.r0 != (whole / gx) * BM ||
+       (whole > 0 && a.dw.dW == nullptr)))
+    return hipErrorInvalidValue;
+  const int64_t units = whole + (gx * gy - whole) * splits;
   if (units > 0x7fffffff) return hipErrorInvalidValue;
   // One workgroup per compute unit (a multiple of the 8 XCDs keeps every
   // workgroup's units on one XCD), or one per unit when there are fewer.
@@ -498,7 +544,7 @@ static hipError_t run16(const GemmArgs& a, hipStream_t s) {
   if (EB == 1 && a.scale == nullptr) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WGM, WGN, A_KM, B_KM, OUT, NS, OCC, SK, NSB, IL, EB>),
                      dim3((unsigned)grid), dim3(64 * WGM * WGN), 0, s, a.A, a.lda, a.B, a.ldb, a.C,
-                     a.ldc, a.M, a.N, a.K, kps, a.split_stride, splits, a.scale);
+                     a.ldc, a.M, a.N, a.K, kps, a.split_stride, splits, a.scale, a.dw);
   return hipGetLastError();
 }
 
@@ -571,8 +617,33 @@ static int gemm_dw_splits(int64_t M, int64_t N, int64_t K, double flops) {
   }
   return best;
 }
-int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K) { return gemm_dw_splits(M, N, K, 1.0e15); }
-int gemm_fp8_dw_splits(int64_t M, int64_t N, int64_t K) { return gemm_dw_splits(M, N, K, 2.0e15); }
+
+// The dW schedule (DwPlan). When the tiles outnumber the CUs, whole rounds of tiles run
+// unsplit and are stored straight into dW, and only the tiles left over are k-split
+// (enough ways to spread them over the CUs, as the estimate above picks): the same
+// rounds of MFMA work as splitting every tile, with partials for the leftover rows
+// alone. Measured at P = 24576, T = 49152: every tile split 7 ways spent 1.85 ms in dW
+// plus 0.11 ms summing 7 partials of 75 MB; 255 whole tiles and 33 split 7 ways
+// (partials of 2816 rows) replace both. Otherwise (fewer tiles than CUs, or more than
+// four column tiles) every tile is split as before.
+static DwPlan gemm_dw_plan(int64_t M, int64_t N, int64_t K, double flops) {
+  DwPlan p;
+  const int64_t nbx = (N + kDwN - 1) / kDwN, nby = (M + kDwM - 1) / kDwM;
+  const int64_t tiles = nbx * nby, slots = cu_count();
+  if (nbx > 4 || tiles <= slots || K < 1024) {
+    p.splits = gemm_dw_splits(M, N, K, flops);
+    return p;
+  }
+  // whole rounds of tiles, trimmed to whole row blocks
+  const int64_t whole = (tiles / slots) * slots / nbx * nbx;
+  const int64_t rest_rows = M - (whole / nbx) * kDwM;
+  p.whole = (int)whole;
+  p.r0 = (whole / nbx) * kDwM;
+  p.splits = rest_rows > 0 ? gemm_dw_splits(rest_rows, N, K, flops) : 1;
+  return p;
+}
+DwPlan gemm_bf16_dw_plan(int64_t M, int64_t N, int64_t K) { return gemm_dw_plan(M, N, K, 1.0e15); }
+DwPlan gemm_fp8_dw_plan(int64_t M, int64_t N, int64_t K) { return gemm_dw_plan(M, N, K, 2.0e15); }
 
 int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K) {
   return dx_wide(N) ? splits_for(M, N, K, 4, true, kWideM, kWideN, 1)
@@ -590,7 +661,10 @@ hipError_t launch_gemm_fp8(Gemm kind, const GemmArgs& a, hipStream_t s) {
       return a.splits > 1
                  ? run16<kTileM, kTileN, 2, 4, false, true, kOutF32Split, 2, 1, 128, 2, true, 1>(a, s)
                  : run16<kTileM, kTileN, 2, 4, false, true, kOutBF16, 2, 1, 128, 2, true, 1>(a, s);
-    case Gemm::DW: return run16<kDwM, kDwN, 4, 2, true, true, kOutF32Split, 2, 1, 128, 2, false, 1>(a, s);
+    case Gemm::DW:
+      return a.dw.whole > 0
+                 ? run16<kDwM, kDwN, 4, 2, true, true, kOutDW, 2, 1, 128, 2, false, 1>(a, s)
+                 : run16<kDwM, kDwN, 4, 2, true, true, kOutF32Split, 2, 1, 128, 2, false, 1>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -611,7 +685,10 @@ hipError_t launch_gemm_bf16(Gemm kind, const GemmArgs& a, hipStream_t s) {
       return a.splits > 1
                  ? run16<kTileM, kTileN, 2, 4, false, false, kOutF32Split, 3, kOcc, 32, 3, true>(a, s)
                  : run16<kTileM, kTileN, 2, 4, false, false, kOutBF16, 3, kOcc, 32, 3, true>(a, s);
-    case Gemm::DW: return run16<kDwM, kDwN, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false>(a, s);
+    case Gemm::DW:
+      return a.dw.whole > 0
+                 ? run16<kDwM, kDwN, 4, 2, true, true, kOutDW, 2, 1, 64, 2, false>(a, s)
+                 : run16<kDwM, kDwN, 4, 2, true, true, kOutF32Split, 2, 1, 64, 2, false>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -52,7 +52,9 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-enum OutMode { kOutBF16 = 0, kOutF32 = 1, kOutF32Split = 2 };
+enum OutMode { kOutBF16 = 0, kOutF32 = 1, kOutF32Split = 2, kOutDW = 3 };
+
+
 
 // Output tile of workgroup `bid` among nby x nbx tiles: XCD-contiguous, grouped.
 __device__ __forceinline__ void tile_of(int bid, int nby, int nbx, int& tm, int& tn) {
@@ -83,6 +85,15 @@ __device__ __forceinline__ int group_rows(int nbx, int64_t tile_bytes) {
   return 8;
 }
 
+// Unit u of `total` renumbered XCD-contiguously: workgroup ids are dealt round-robin
+// over the XCDs, so u % kNumXcd is the unit's XCD (any constant shift of u keeps the
+// XCD groups intact); the XCD's units get consecutive numbers.
+__device__ __forceinline__ int xcd_order(int u, int total) {
+  const int q = total / kNumXcd, rem = total % kNumXcd;
+  const int x = u % kNumXcd, i = u / kNumXcd;
+  return x < rem ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
+}
+
 // Tile and k-range of unit u among nby x nbx tiles x `splits` k-ranges. Units are
 // renumbered XCD-contiguously (workgroup ids are dealt round-robin over the XCDs) with the
 // k-range outermost, so each XCD works on one k-range. Within a k-range, tiles go
@@ -91,10 +102,7 @@ __device__ __forceinline__ int group_rows(int nbx, int64_t tile_bytes) {
 __device__ __forceinline__ void unit_of(int u, int nby, int nbx, int splits, int gm, int& tm,
                                         int& tn, int& split) {
   const int ntiles = nby * nbx;
-  const int total = ntiles * splits;
-  const int q = total / kNumXcd, rem = total % kNumXcd;
-  const int x = u % kNumXcd, i = u / kNumXcd;
-  const int lid = x < rem ? x * (q + 1) + i : rem * (q + 1) + (x - rem) * q + i;
+  const int lid = xcd_order(u, ntiles * splits);
   split = lid / ntiles;
   const int t = lid - split * ntiles;
   if (nbx <= 4) {
@@ -179,6 +187,41 @@ __device__ __forceinline__ void store_acc(f32x16_t (&acc)[TM][TN], void* __restr
             *reinterpret_cast<float4*>(out + row * ldc + col) =
                 make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
         }
+    }
+  }
+}
+
+// bf16 output of one wave into rows picked by `rowmap` (output row r goes to row
+// rowmap[r], or r when rowmap is null): the layout of store_acc's bf16 case, with the
+// destination row looked up once per 32-row block (rows >= M are not stored).
+template <int TM, int TN>
+__device__ __forceinline__ void store_acc_rows_bf16(f32x16_t (&acc)[TM][TN], void* __restrict__ Cout,
+                                                    int64_t ldc, const int32_t* __restrict__ rowmap,
+                                                    int64_t M, int64_t N, int64_t rbase,
+                                                    int64_t cbase, int half) {
+  const int64_t ncols = (N + 7) / 8 * 8;
+  bf16_t* out = static_cast<bf16_t*>(Cout);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = rbase + i * 32;
+    const int64_t dst = row < M ? (rowmap ? (int64_t)rowmap[row] : row) : 0;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const int g0 = 4 * (2 * gp), g1 = 4 * (2 * gp + 1);
+        uint32_t e0 = pack_bf16x2(acc[i][j][g0 + 0], acc[i][j][g0 + 1]);
+        uint32_t e1 = pack_bf16x2(acc[i][j][g0 + 2], acc[i][j][g0 + 3]);
+        uint32_t o0 = pack_bf16x2(acc[i][j][g1 + 0], acc[i][j][g1 + 1]);
+        uint32_t o1 = pack_bf16x2(acc[i][j][g1 + 2], acc[i][j][g1 + 3]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(e0, o0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(e1, o1, false, false);
+        e0 = s0[0]; o0 = s0[1];
+        e1 = s1[0]; o1 = s1[1];
+        const int64_t col = cbase + j * 32 + 8 * (2 * gp + half);
+        if (row < M && col < ncols)
+          *reinterpret_cast<uint4*>(out + dst * ldc + col) = make_uint4(e0, e1, o0, o1);
+      }
     }
   }
 }

@@ -256,6 +256,21 @@ __device__ __forceinline__ void amax_bf16_block(const uint4* __restrict__ x, int
 
 // GEMMs. Matrices row-major; see gemm.hip for the operand conventions.
 enum class Gemm { Logits, DX, DW };
+// The dW product's two kinds of unit (kOutDW). The tile order is row-major over
+// nbx <= 4 column tiles; its first `whole` tiles (a multiple of nbx: whole row blocks,
+// rows [0, r0)) are computed over all of K by one unit each and stored as bf16 straight
+// into the dense gradient, at row rowmap[row] (the candidate class; row itself when
+// rowmap is null). The other tiles are k-split as usual into fp32 partial slabs of rows
+// [r0, M) (partial row = row - r0), which a reduction sums and scatters. Whole units fill
+// the chip in whole rounds and only the tiles left over are split, so the partial round
+// trip covers those alone.
+struct DwOut {
+  void* dW = nullptr;             // bf16 rows of ldw elements
+  int64_t ldw = 0;
+  const int32_t* rowmap = nullptr;
+  int whole = 0;
+  int64_t r0 = 0;
+};
 struct GemmArgs {
   const void* A;
   int64_t lda;
@@ -267,11 +282,19 @@ struct GemmArgs {
   int splits;            // split-K factor (fp32 partial slabs when > 1)
   int64_t split_stride;  // elements between split slabs of C
   const float* scale = nullptr;  // e4m3 products: device factor applied before the store
+  DwOut dw{};                    // dW with whole tiles (dw.whole > 0): see DwOut
 };
-// k-splits (1 = no split) of the bf16 dW and dX products, for the tile shapes their
-// launches use; the fp32 products use gemm_f32_splits.
-int gemm_bf16_dw_splits(int64_t M, int64_t N, int64_t K);
-int gemm_fp8_dw_splits(int64_t M, int64_t N, int64_t K);
+// The schedule of the bf16 / e4m3 dW product (M = P, N = d, K = T): `whole` tiles
+// computed whole and stored into dW (rows [0, r0) of the candidate order), the rest
+// k-split `splits` ways into fp32 partials of rows [r0, M). whole = 0, r0 = 0: every
+// tile split (splits = 1: one fp32 slab).
+struct DwPlan {
+  int splits = 1;
+  int whole = 0;
+  int64_t r0 = 0;
+};
+DwPlan gemm_bf16_dw_plan(int64_t M, int64_t N, int64_t K);
+DwPlan gemm_fp8_dw_plan(int64_t M, int64_t N, int64_t K);
 int gemm_fp8_dx_splits(int64_t M, int64_t N, int64_t K);
 int gemm_bf16_dx_splits(int64_t M, int64_t N, int64_t K);
 int gemm_f32_splits(int64_t M, int64_t N, int64_t K);

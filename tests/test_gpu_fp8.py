@@ -21,6 +21,9 @@ CASES = [
     (1000, 256, 3000, 1500, False, 0.0, 7),
     (64, 768, 50304, 10240, True, 0.0, 20011),  # full vocabulary and hidden size
     (2050, 96, 2500, 1601, False, 0.0, 3),
+    # more dW tiles than compute units: whole tiles stored straight into dW, the rest k-split
+    (1024, 16, 70000, 66000, True, 0.0, 3),
+    (1024, 16, 66000, 0, True, 0.0, 1),
     (1, 64, 100, 40, True, 0.0, 3),             # one token
     # the size limits of include/sampled_ce.h
     (64, 64, 131072, 40000, True, 0.0, 99991),  # V = SCE_MAX_V_SAMPLED

@@ -26,6 +26,10 @@ CASES = [
     (64, 768, 50304, 10240, "bf16", True, 0.0, 20011),  # full vocabulary and hidden size
     (2050, 96, 2500, 1601, "bf16", False, 0.0, 3),
     (700, 384, 3000, 1111, "bf16", True, 0.05, 7),     # d % 192 == 0: the 256 x 192 dX tiles, ragged
+    # more dW tiles than compute units: whole tiles stored straight into dW, the rest k-split
+    (2048, 16, 70000, 66000, "bf16", True, 0.0, 3),     # 258 tiles of one column, rows via C
+    (2048, 16, 66000, 0, "bf16", True, 0.0, 1),         # the same in the full softmax
+    (1100, 1024, 20000, 17000, "bf16", False, 0.0, 3),  # four column tiles, ragged last row block
     # the size limits of include/sampled_ce.h
     (64, 64, 131072, 40000, "bf16", True, 0.0, 99991),  # V = SCE_MAX_V_SAMPLED
     (48, 64, 1048576, 0, "bf16", True, 0.0, 1),          # V = SCE_MAX_V: rows for the streaming CE
