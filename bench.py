@@ -37,11 +37,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_work(w, P_eff, e4m3=False):
+def dw_split_rows(w, P_eff, cus):
+    """Rows of dW_C that go through the k-split reduction (the scatter stage). The dW
+    product (256 x 256 tiles, M = P_eff, N = d, K = T) stores whole rounds of tiles
+    straight into dW when its tiles outnumber the CUs, its column tiles are at most 4
+    and T >= 1024 (whole rounds trimmed to whole row blocks); the other rows are
+    k-split. The fp32 step splits every row."""
+    nbx, nby = -(-w.d // 256), -(-P_eff // 256)
+    tiles = nbx * nby
+    if w.dtype != "bf16" or nbx > 4 or tiles <= cus or w.T < 1024:
+        return P_eff
+    whole = (tiles // cus) * cus // nbx * nbx
+    return P_eff - (whole // nbx) * 256
+
+
+def stage_work(w, P_eff, e4m3=False, cus=256):
     """Algorithmic work of one launch of each stage: (kind, amount)."""
     es = 2 if w.dtype == "bf16" else 4
     ldz = (P_eff + 7) // 8 * 8
     flops = 2.0 * w.T * P_eff * w.d
+    split_rows = dw_split_rows(w, P_eff, cus)
     # read Z once, write dZ once (e4m3 step: read bf16 Z, write the e4m3 gradient), plus
     # labels and the row loss
     ce_bytes = (w.T * ldz * 3.0 if e4m3 else 2.0 * w.T * ldz * es) + w.T * 12
@@ -50,9 +65,10 @@ def stage_work(w, P_eff, e4m3=False):
         "dx": ("mfma", flops),
         "dw": ("mfma", flops),
         "ce": ("hbm", ce_bytes),
-        # read the fp32 candidate-row gradient once, write the candidate rows of dense dW
-        # (the rows outside C are cleared in the candidates stage)
-        "scatter": ("hbm", P_eff * w.d * (4.0 + (2 if e4m3 else es))),
+        # read the fp32 gradient of the k-split candidate rows once, write those rows of
+        # dense dW (the dW product stores the other candidate rows; the rows outside C are
+        # cleared in the candidates stage)
+        "scatter": ("hbm", split_rows * w.d * (4.0 + (2 if e4m3 else es))),
         # sum the fp32 k-split partials of dX into dX (bytes of a 2-way split)
         "dx_reduce": ("hbm", 2 * w.T * w.d * 4.0 + w.T * w.d * es),
     }
@@ -383,7 +399,8 @@ def main():
     b = Bench(w, dev, e4m3)
     b.prepare(w.P)
     P_eff = w.P if w.P else w.V
-    work = stage_work(w, P_eff, e4m3)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    work = stage_work(w, P_eff, e4m3, cus)
     settled = b.settle(w.P)
     log(f"[bench] {settled} untimed steps while the clock settles")
     stage_ms = b.stage_ms(w.P, max(20, min(args.steps, 50)))
@@ -423,6 +440,11 @@ def main():
     if achievable:
         ref = achievable["gemm_tflops"] if roof["bound"] == "mfma" else achievable["copy_gbs"]
         achievable["dominant_frac"] = round(roof["achieved"] / ref, 4)
+        if ptype == "bf16":
+            lib = library_same_shapes(torch, dev, w)
+            for k in lib:
+                lib[k]["ours_us"] = round(stage_ms[k] * 1e3, 1)
+            achievable["library_same_shapes"] = lib
         log(f"[bench] achievable on this GPU: {achievable}")
 
     full_cmp = None
@@ -490,7 +512,7 @@ def other_config(w, dev, e4m3, args, torch):
     b = Bench(w, dev, e4m3)
     b.prepare(w.P)
     P_eff = w.P if w.P else w.V
-    work = stage_work(w, P_eff, e4m3)
+    work = stage_work(w, P_eff, e4m3, torch.cuda.get_device_properties(dev).multi_processor_count)
     settled = b.settle(w.P)
     stage_ms = b.stage_ms(w.P, 12)
     stages = stage_table(stage_ms, work, ptype)
@@ -542,6 +564,27 @@ def measured_peaks(torch, dev, ptype):
     return {"copy_gbs": round(2.0 * n / (copy_ms * 1e-3) / 1e9, 1),
             "gemm_tflops": round(2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
             "gemm": f"{m}^3 {ptype}, vendor library"}
+
+
+def library_same_shapes(torch, dev, w):
+    """The vendor library (hipBLASLt through torch.matmul, bf16, 2-D products) on the
+    step's three products at this workload's shapes and operand layouts: logits
+    x [T, d] @ W_C^T, dX dZ [T, P] @ W_C [P, d], dW dZ^T @ x; microseconds each and the
+    fraction of the bf16 peak."""
+    T, d, P = w.T, w.d, (w.P or w.V)
+    x = torch.randn(T, d, device=dev, dtype=torch.bfloat16)
+    Wc = (0.02 * torch.randn(P, d, device=dev)).to(torch.bfloat16)
+    Z = (1e-4 * torch.randn(T, P, device=dev)).to(torch.bfloat16)
+    fl = 2.0 * T * P * d
+    out = {}
+    for name, fn in (("logits", lambda: torch.matmul(x, Wc.t())), ("dx", lambda: torch.matmul(Z, Wc)),
+                     ("dw", lambda: torch.matmul(Z.t(), x))):
+        ms = _time_ms(fn, reps=20, warmup=3)
+        out[name] = {"us": round(ms * 1e3, 1),
+                     "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+    del x, Wc, Z
+    torch.cuda.empty_cache()
+    return out
 
 
 def _time_ms(fn, reps=50, warmup=10):
