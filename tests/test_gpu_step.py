@@ -161,3 +161,25 @@ def test_label_out_of_range_is_flagged_not_faulted():
     y = np.arange(T, dtype=np.int64)  # 64 distinct targets > P = 50
     out = _step(x, W, y, None, 50, 7, 0, "bf16")
     assert out["aux"].cpu().numpy()[3] & binding.DEV_TOO_MANY_TARGETS
+
+
+def test_whole_tile_dw_deterministic_and_p0_equals_pv():
+    """A dW product with more tiles than compute units (whole tiles stored by the product,
+    the rest reduced): repeated calls into outputs pre-filled with garbage give the same
+    bits, and P = V gives the bits of P = 0."""
+    T, d, V = 2048, 16, 66000
+    print(f"whole-tile dW T={T} d={d} V={V}", flush=True)
+    x, W, y, p = synth.small_case(41, T, d, V, "bf16", prefix=True, ignore_frac=0.05)
+    xd, Wd, yd, pd = to_dev(x, "bf16"), to_dev(W, "bf16"), labels_dev(y), labels_dev(p)
+    first = binding.forward_backward(xd, Wd, yd, pd, 0, 1, 0, want_rows=True)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in first.items() if torch.is_tensor(v)}
+    for v in first.values():
+        if torch.is_tensor(v):
+            v.fill_(7)
+    again = binding.forward_backward(xd, Wd, yd, pd, 0, 1, 0, outputs=first, want_rows=True)
+    pv = binding.forward_backward(xd, Wd, yd, pd, V, 1, 0, want_rows=True)
+    torch.cuda.synchronize()
+    for k in ("loss", "dX", "dW", "row_lse", "row_loss", "target_pos", "prefix_pos"):
+        assert torch.equal(again[k], ref[k]), k
+        assert torch.equal(pv[k], ref[k]), k
