@@ -267,6 +267,25 @@ SCE_API sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8
                                            size_t workspace_bytes, void* stream);
 
 /*
+ * sampled_ce_forward_backward_fp8_prebuilt -- the e4m3 step from a candidate set built
+ * before, the page's own arrangement ("sampled_softmax.py": the set is built on a CPU
+ * worker and staged to the GPU, SampledSoftmax; the lm_head is the e4m3 cache). The
+ * same results as sampled_ce_forward_backward_fp8 given the same set, bit for bit.
+ *   x, W8, w_scale, w_scale_dev, T, d, V, loss, dX, dW, row_lse_out, row_loss_out,
+ *   aux_out, scales_out, workspace (sce_workspace_size(T, d, V, P, SCE_E4M3)), stream:
+ *         as in sampled_ce_forward_backward_fp8.
+ *   candidates, target_pos, prefix_pos, build_aux, P (>= 1): as in
+ *         sampled_ce_forward_backward_prebuilt (device memory, validated on the device;
+ *         prefix_pos NULL: no prefix targets, n_max = 1).
+ */
+SCE_API sce_status sampled_ce_forward_backward_fp8_prebuilt(
+    const void* x, const void* W8, float w_scale, const float* w_scale_dev,
+    const int32_t* candidates, const int32_t* target_pos, const int32_t* prefix_pos,
+    const int64_t* build_aux, int64_t T, int64_t d, int64_t V, int64_t P, float* loss, void* dX,
+    void* dW, float* row_lse_out, float* row_loss_out, int64_t* aux_out, float* scales_out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * sce_refresh_e4m3_cache -- rebuilds the e4m3 lm_head cache the fp8 step reads from the
  * bf16 weights ("sampled_softmax.py" refreshes this cache before it gathers candidate
  * rows; the page does not give the encoding). Per-tensor scale, the largest magnitude

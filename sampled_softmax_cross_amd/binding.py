@@ -22,7 +22,8 @@ STATUS = {0: "SCE_OK", 1: "SCE_EINVAL", 2: "SCE_EWORKSPACE", 3: "SCE_EHIP"}
 EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sce_build_candidates_noalloc",
            "sce_build_candidates_host",
            "sampled_ce_forward_backward", "sampled_ce_forward_backward_prebuilt",
-           "sampled_ce_forward_backward_fp8", "sce_refresh_e4m3_cache",
+           "sampled_ce_forward_backward_fp8", "sampled_ce_forward_backward_fp8_prebuilt",
+           "sce_refresh_e4m3_cache",
            "sce_ce_rows_workspace_size", "sce_ce_rows", "sce_gather_rows",
            "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
 STAGES = ("candidates", "logits", "ce", "dx", "dx_reduce", "dw", "scatter")
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
                                                     i64, i64, i64, p, p, p, p, p, p, p, p, p, p,
                                                     p, sz, p]
     lib.sampled_ce_forward_backward_fp8.restype = i32
+    lib.sampled_ce_forward_backward_fp8_prebuilt.argtypes = [p, p, ctypes.c_float, p, p, p, p, p,
+                                                             i64, i64, i64, i64, p, p, p, p, p,
+                                                             p, p, p, sz, p]
+    lib.sampled_ce_forward_backward_fp8_prebuilt.restype = i32
     lib.sce_refresh_e4m3_cache.argtypes = [p, i64, i64, p, p, p, p, sz, p]
     lib.sce_refresh_e4m3_cache.restype = i32
     lib.sce_ce_rows_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
@@ -149,7 +154,7 @@ def build_candidates(targets, prefix_targets, V, P, stride, offset, *, want_voca
     if rc != 0:
         raise SceError("sce_build_candidates", rc)
     return dict(C=C, target_pos=tpos[:T], prefix_pos=ppos[:T], vocab_pos=vpos, aux=aux,
-                _tpos=tpos, _ppos=ppos)
+                _tpos=tpos, _ppos=ppos, has_prefix=prefix_targets is not None)
 
 
 def build_candidates_host(targets, prefix_targets, V, P, stride, offset, *, outputs=None):
@@ -206,7 +211,7 @@ def build_candidates_noalloc(targets, prefix_targets, V, P, stride, offset, *,
     if rc != 0:
         raise SceError("sce_build_candidates_noalloc", rc)
     return dict(C=C, target_pos=tpos[:T], prefix_pos=None if ppos is None else ppos[:T],
-                vocab_pos=vpos, aux=aux)
+                vocab_pos=vpos, aux=aux, has_prefix=prefix_targets is not None)
 
 
 def forward_backward(x, W, targets, prefix_targets, P, stride, offset, *, outputs=None, ws=None,
@@ -311,6 +316,68 @@ def forward_backward_prebuilt(x, W, cand, *, outputs=None, ws=None, want_rows=Fa
     return o
 
 
+def _scale_args(w_scale, dev):
+    """(host scale, device scale tensor or None) from a float or a float32 device tensor."""
+    if isinstance(w_scale, torch.Tensor):
+        if w_scale.dtype != torch.float32 or w_scale.device != dev or w_scale.numel() < 1:
+            raise ValueError("a device w_scale is a float32 tensor on x's device")
+        return 1.0, w_scale
+    return float(w_scale), None
+
+
+def forward_backward_fp8_prebuilt(x, W8, w_scale, cand, *, outputs=None, ws=None,
+                                  want_rows=False):
+    """The e4m3 step from a candidate set built beforehand (`cand` as for
+    forward_backward_prebuilt); x, W8 and w_scale as for forward_backward_fp8. Returns
+    its keys except C and the positions. The gradient's scale depends on whether the
+    microbatch has prefix targets (n_max): a set built without them (cand["has_prefix"]
+    False, or prefix_pos None) is stepped without prefix positions, as the one-call step
+    is."""
+    lib = load_library()
+    dev = x.device
+    T, d = x.shape
+    V = W8.shape[0]
+    P = cand["C"].shape[0]
+    if x.dtype != torch.bfloat16 or W8.shape[1] != d or W8.element_size() != 1:
+        raise ValueError("x must be bf16 and W8 one byte per element with x's hidden size")
+    for name, t in (("x", x), ("W8", W8)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for k in ("C", "target_pos", "prefix_pos"):
+        t = cand.get(k)
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{k} must be contiguous int32")
+    o = dict(outputs or {})
+    if "loss" not in o:
+        o["loss"] = torch.empty(1, dtype=torch.float32, device=dev)
+    if "dX" not in o:
+        o["dX"] = torch.empty_like(x)
+    if "dW" not in o:
+        o["dW"] = torch.empty(V, d, dtype=torch.bfloat16, device=dev)
+    if "aux" not in o:
+        o["aux"] = torch.empty(4, dtype=torch.int64, device=dev)
+    if "scales" not in o:
+        o["scales"] = torch.empty(2, dtype=torch.float32, device=dev)
+    if want_rows:
+        for k in ("row_lse", "row_loss"):
+            if k not in o:
+                o[k] = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+    host_scale, dev_scale = _scale_args(w_scale, dev)
+    nbytes = workspace_size(T, d, V, P, SCE_E4M3)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    rc = lib.sampled_ce_forward_backward_fp8_prebuilt(
+        _ptr(x), _ptr(W8), ctypes.c_float(host_scale), _ptr(dev_scale), _ptr(cand["C"]),
+        _ptr(cand["target_pos"]), _ptr(cand.get("prefix_pos") if cand.get("has_prefix", True) else None),
+        _ptr(cand.get("aux")), T, d, V, P,
+        _ptr(o["loss"]), _ptr(o["dX"]), _ptr(o["dW"]), _ptr(o.get("row_lse")),
+        _ptr(o.get("row_loss")), _ptr(o["aux"]), _ptr(o["scales"]), _ptr(ws), ws.numel(),
+        _stream(dev))
+    if rc != 0:
+        raise SceError("sampled_ce_forward_backward_fp8_prebuilt", rc)
+    return o
+
+
 def forward_backward_fp8(x, W8, w_scale, targets, prefix_targets, P, stride, offset, *,
                          outputs=None, ws=None, want_rows=False):
     """One sampled-CE step with e4m3 product operands. x [T,d] bf16, W8 [V,d] the lm_head
@@ -355,12 +422,7 @@ def forward_backward_fp8(x, W8, w_scale, targets, prefix_targets, P, stride, off
     nbytes = workspace_size(T, d, V, P, SCE_E4M3)
     if ws is None:
         ws = workspace(nbytes, dev)
-    if isinstance(w_scale, torch.Tensor):
-        if w_scale.dtype != torch.float32 or w_scale.device != dev or w_scale.numel() < 1:
-            raise ValueError("a device w_scale is a float32 tensor on x's device")
-        host_scale, dev_scale = 1.0, w_scale
-    else:
-        host_scale, dev_scale = float(w_scale), None
+    host_scale, dev_scale = _scale_args(w_scale, dev)
     rc = lib.sampled_ce_forward_backward_fp8(
         _ptr(x), _ptr(W8), ctypes.c_float(host_scale), _ptr(dev_scale), _ptr(targets), _ptr(prefix_targets), T, d, V,
         P, stride, offset, _ptr(o["loss"]), _ptr(o["dX"]), _ptr(o["dW"]), _ptr(o["C"]),

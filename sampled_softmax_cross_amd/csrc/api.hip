@@ -468,44 +468,16 @@ sce_status sampled_ce_forward_backward_prebuilt(const void* x, const void* W,
   return hip_status(e);
 }
 
-sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float w_scale,
-                                           const float* w_scale_dev,
-                                           const int64_t* targets, const int64_t* prefix_targets,
-                                           int64_t T, int64_t d, int64_t V, int64_t P,
-                                           int64_t stride, int64_t offset, float* loss, void* dX,
-                                           void* dW, int32_t* candidates_out,
-                                           int32_t* target_pos_out, int32_t* prefix_pos_out,
-                                           float* row_lse_out, float* row_loss_out,
-                                           int64_t* aux_out, float* scales_out, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
-  sce_status st = check_sizes(T, d, V, P, SCE_E4M3, true);
-  if (st != SCE_OK) return st;
-  if (w_scale_dev == nullptr && (!(w_scale > 0.f) || w_scale > 3.0e38f))
-    return SCE_EINVAL;  // also rejects NaN; a device scale is checked on the device
-  if (w_scale_dev != nullptr && (reinterpret_cast<uintptr_t>(w_scale_dev) & 3) != 0)
-    return SCE_EINVAL;
-  if (W8 == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
-  if (T > 0 && (x == nullptr || targets == nullptr || dX == nullptr)) return SCE_EINVAL;
-  if ((x && !aligned16(x)) || !aligned16(W8) || (dX && !aligned16(dX)) || !aligned16(dW))
-    return SCE_EINVAL;
-  int64_t s = 1;
-  if (P > 0) {
-    s = mod64(stride, V);
-    if (gcd64(s, V) != 1) return SCE_EINVAL;
-  }
-  const Plan p = make_plan(T, d, V, P, SCE_E4M3, true);
-  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
-
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
-  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
-  int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
-  int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
-  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
-  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+// The e4m3 step after its candidate stage: x's quantisation (from the max|x| partials
+// the candidate launch left), the three e4m3 products, the CE writing the e4m3 gradient,
+// the reductions and the loss. n_max = 2 with prefix targets, else 1.
+static hipError_t enqueue_products_fp8(const Plan& p, char* ws, const void* x, const void* W8,
+                                       float w_scale, const float* w_scale_dev, int64_t T,
+                                       int64_t d, int64_t P, int n_max, int32_t* counters,
+                                       int32_t* cand, int32_t* tpos, int32_t* ppos,
+                                       float* row_loss, float* row_lse_out, float* loss, void* dX,
+                                       void* dW, int64_t* aux_out, float* scales_out,
+                                       int amax_parts, StageMarks& marks, hipStream_t hs) {
   float* scales = reinterpret_cast<float*>(ws + p.scales);
   void* Z = ws + p.z;
   uint8_t* x8 = reinterpret_cast<uint8_t*>(ws + p.x8);
@@ -513,17 +485,8 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   float* part = reinterpret_cast<float*>(ws + p.part);
   const void* WC = P > 0 ? static_cast<const void*>(ws + p.wc) : W8;
 
-  StageMarks marks(hs);
-  marks.mark(SCE_STAGE_CANDIDATES);
-  int amax_parts = 0;  // max|x| partials, taken beside the candidate build
-  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
-                                   (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
-                                   tpos, ppos,
-                                   W8, (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2), hs,
-                                   x, T * d, &amax_parts);
-  if (e == hipSuccess)
-    e = launch_quant_x(x, T * d, counters, w_scale, w_scale_dev, x8, scales, scales_out, hs,
-                       amax_parts);
+  hipError_t e = launch_quant_x(x, T * d, counters, w_scale, w_scale_dev, x8, scales, scales_out,
+                                hs, amax_parts);
   marks.mark(SCE_STAGE_LOGITS);
   if (e == hipSuccess && T > 0) {
     GemmArgs g{x8, d, WC, p.ldwc, Z, p.ldz, T, p.Peff, d, 1, 0, scales + kScaleLogits};
@@ -531,7 +494,7 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   }
   marks.mark(SCE_STAGE_CE);
   if (e == hipSuccess) {
-    const G8Out go{g8, p.ldg, prefix_targets ? 2 : 1, scales, scales_out};
+    const G8Out go{g8, p.ldg, n_max, scales, scales_out};
     e = launch_ce_rows_g8(Z, p.ldz, (int)T, (int)p.Peff, tpos, ppos, counters, row_loss,
                           row_lse_out, go, hs);
   }
@@ -568,6 +531,107 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
                             P > 0 ? dW : static_cast<char*>(dW) + r0 * d * 2, &fin, hs);
   }
   marks.mark(SCE_NUM_STAGES);
+  return e;
+}
+
+// Host checks shared by the e4m3 entry points.
+static sce_status check_fp8(const void* x, const void* W8, float w_scale,
+                            const float* w_scale_dev, const void* labels, int64_t T, int64_t d,
+                            int64_t V, int64_t P, const float* loss, const void* dX,
+                            const void* dW) {
+  const sce_status st = check_sizes(T, d, V, P, SCE_E4M3, true);
+  if (st != SCE_OK) return st;
+  if (w_scale_dev == nullptr && (!(w_scale > 0.f) || w_scale > 3.0e38f))
+    return SCE_EINVAL;  // also rejects NaN; a device scale is checked on the device
+  if (w_scale_dev != nullptr && (reinterpret_cast<uintptr_t>(w_scale_dev) & 3) != 0)
+    return SCE_EINVAL;
+  if (W8 == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
+  if (T > 0 && (x == nullptr || labels == nullptr || dX == nullptr)) return SCE_EINVAL;
+  if ((x && !aligned16(x)) || !aligned16(W8) || (dX && !aligned16(dX)) || !aligned16(dW))
+    return SCE_EINVAL;
+  return SCE_OK;
+}
+
+sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float w_scale,
+                                           const float* w_scale_dev,
+                                           const int64_t* targets, const int64_t* prefix_targets,
+                                           int64_t T, int64_t d, int64_t V, int64_t P,
+                                           int64_t stride, int64_t offset, float* loss, void* dX,
+                                           void* dW, int32_t* candidates_out,
+                                           int32_t* target_pos_out, int32_t* prefix_pos_out,
+                                           float* row_lse_out, float* row_loss_out,
+                                           int64_t* aux_out, float* scales_out, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  sce_status st = check_fp8(x, W8, w_scale, w_scale_dev, targets, T, d, V, P, loss, dX, dW);
+  if (st != SCE_OK) return st;
+  int64_t s = 1;
+  if (P > 0) {
+    s = mod64(stride, V);
+    if (gcd64(s, V) != 1) return SCE_EINVAL;
+  }
+  const Plan p = make_plan(T, d, V, P, SCE_E4M3, true);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
+  int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
+  int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+
+  StageMarks marks(hs);
+  marks.mark(SCE_STAGE_CANDIDATES);
+  int amax_parts = 0;  // max|x| partials, taken beside the candidate build
+  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
+                                   (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
+                                   tpos, ppos,
+                                   W8, (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2), hs,
+                                   x, T * d, &amax_parts);
+  if (e == hipSuccess)
+    e = enqueue_products_fp8(p, ws, x, W8, w_scale, w_scale_dev, T, d, P,
+                             prefix_targets ? 2 : 1, counters, cand, tpos, ppos, row_loss,
+                             row_lse_out, loss, dX, dW, aux_out, scales_out, amax_parts, marks,
+                             hs);
+  return hip_status(e);
+}
+
+sce_status sampled_ce_forward_backward_fp8_prebuilt(
+    const void* x, const void* W8, float w_scale, const float* w_scale_dev,
+    const int32_t* candidates, const int32_t* target_pos, const int32_t* prefix_pos,
+    const int64_t* build_aux, int64_t T, int64_t d, int64_t V, int64_t P, float* loss, void* dX,
+    void* dW, float* row_lse_out, float* row_loss_out, int64_t* aux_out, float* scales_out,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  sce_status st = check_fp8(x, W8, w_scale, w_scale_dev, target_pos, T, d, V, P, loss, dX, dW);
+  if (st != SCE_OK) return st;
+  if (P < 1 || candidates == nullptr) return SCE_EINVAL;  // a sampled candidate set only
+  const Plan p = make_plan(T, d, V, P, SCE_E4M3, true);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* cand = reinterpret_cast<int32_t*>(ws + p.cand);
+  int32_t* tpos = reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+
+  StageMarks marks(hs);
+  marks.mark(SCE_STAGE_CANDIDATES);
+  int amax_parts = 0;
+  hipError_t e = launch_candidates_prebuilt(candidates, target_pos, prefix_pos, build_aux, (int)T,
+                                            (int)V, (int)P, counters, cand, bits, tpos, ppos, W8,
+                                            (int)d, ws + p.wc, (int)p.ldwc, dW, (int)(d * 2),
+                                            nullptr, 0, hs, x, T * d, &amax_parts);
+  if (e == hipSuccess)
+    e = enqueue_products_fp8(p, ws, x, W8, w_scale, w_scale_dev, T, d, P, prefix_pos ? 2 : 1,
+                             counters, cand, tpos, ppos, row_loss, row_lse_out, loss, dX, dW,
+                             aux_out, scales_out, amax_parts, marks, hs);
   return hip_status(e);
 }
 

@@ -309,7 +309,13 @@ __global__ __launch_bounds__(256) void k_remap_gather(
 // aux when given (else -1, -1, 0).
 __global__ __launch_bounds__(kBuildThreads) void k_cand_prebuilt(
     const int32_t* __restrict__ C_in, int V, int P, const int64_t* __restrict__ build_aux,
-    int32_t* __restrict__ counters, int32_t* __restrict__ C, uint32_t* __restrict__ bits) {
+    int32_t* __restrict__ counters, int32_t* __restrict__ C, uint32_t* __restrict__ bits,
+    const uint4* __restrict__ amax_x, int64_t amax_nvec) {
+  // Blocks past the first: the e4m3 step's max|x| partials, as beside the device build.
+  if (blockIdx.x > 0) {
+    amax_bf16_block(amax_x, amax_nvec, (int)blockIdx.x - 1, (int)gridDim.x - 1, counters);
+    return;
+  }
   extern __shared__ uint32_t mark[];
   __shared__ int scratch[kBuildThreads / kWave + 1];
   const int W = (V + 31) >> 5;
@@ -384,11 +390,14 @@ hipError_t launch_candidates_prebuilt(const int32_t* C_in, const int32_t* tpos_i
                                       int V, int P, int32_t* counters, int32_t* C, uint32_t* bits,
                                       int32_t* target_pos, int32_t* prefix_pos, const void* W,
                                       int row_bytes, void* WC, int wc_row_bytes, void* dW,
-                                      int dw_row_bytes, void* WT, int64_t ldt, hipStream_t s) {
+                                      int dw_row_bytes, void* WT, int64_t ldt, hipStream_t s,
+                                      const void* amax_x, int64_t amax_n, int* amax_parts) {
   if (P < 1 || V > kMaxBitmapClasses) return hipErrorInvalidValue;
   const size_t lds = (size_t)((V + 31) / 32) * sizeof(uint32_t);
-  hipLaunchKernelGGL(k_cand_prebuilt, dim3(1), dim3(kBuildThreads), lds, s, C_in, V, P, build_aux,
-                     counters, C, bits);
+  const int agrid = amax_n >= 0 ? amax_block_count(amax_n / 8) : 0;
+  if (amax_parts) *amax_parts = agrid;
+  hipLaunchKernelGGL(k_cand_prebuilt, dim3(1 + agrid), dim3(kBuildThreads), lds, s, C_in, V, P,
+                     build_aux, counters, C, bits, static_cast<const uint4*>(amax_x), amax_n / 8);
   // the remap launch in its positions mode: the same gather (with the transpose), zero rows
   // and label counting as after a build, with the positions copied instead of derived
   const int remap_blocks = (T + 255) / 256;

@@ -31,13 +31,16 @@ hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s
 // [P] ascending classes and the label positions tpos_in / ppos_in (ppos_in may be null)
 // are checked and copied to C / target_pos / prefix_pos, the counters set (distinct count,
 // next offset and device bits from build_aux when given), then the same gather, transpose
-// and zero rows as launch_candidates.
+// and zero rows as launch_candidates. amax_n >= 0: the e4m3 step's max|x| partials over
+// amax_x (amax_n bf16 values) by extra workgroups of the first launch, as there.
 hipError_t launch_candidates_prebuilt(const int32_t* C_in, const int32_t* tpos_in,
                                       const int32_t* ppos_in, const int64_t* build_aux, int T,
                                       int V, int P, int32_t* counters, int32_t* C, uint32_t* bits,
                                       int32_t* target_pos, int32_t* prefix_pos, const void* W,
                                       int row_bytes, void* WC, int wc_row_bytes, void* dW,
-                                      int dw_row_bytes, void* WT, int64_t ldt, hipStream_t s);
+                                      int dw_row_bytes, void* WT, int64_t ldt, hipStream_t s,
+                                      const void* amax_x = nullptr, int64_t amax_n = -1,
+                                      int* amax_parts = nullptr);
 
 // Row gather, one block of 256 lanes per kGatherRows rows: 32 lanes per row, each
 // moving whole 16-byte vectors, every load of a lane issued before its stores. Rows of

@@ -161,6 +161,28 @@ def test_fp8_host_checks(lib):
 
 
 
+def test_fp8_prebuilt_host_checks(lib):
+    f = lib.sampled_ce_forward_backward_fp8_prebuilt
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    args = dict(x=fake, W8=fake, ws=ctypes.c_float(0.01), wsd=None, c=fake, tp=fake, pp=None,
+                aux_in=None, T=4, d=16, V=16, P=4, loss=fake, dX=fake, dW=fake, lse=None, rl=None,
+                aux=None, sc=None, wsp=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    assert call() == 2                                   # no workspace
+    assert call(P=0) == 1                                # a sampled set only
+    assert call(c=None) == 1
+    assert call(tp=None) == 1                            # T > 0 needs the target positions
+    assert call(ws=ctypes.c_float(0.0)) == 1             # host scale must be > 0
+    assert call(ws=ctypes.c_float(0.0), wsd=fake) == 2   # a device scale replaces it
+    assert call(d=8) == 1                                # d % 16 != 0
+    assert call(x=ctypes.c_void_p((1 << 20) + 8)) == 1   # misaligned
+    assert call(V=binding.MAX_V_SAMPLED + 1, P=4) == 1   # the sampled path's V limit
+
+
 def test_refresh_host_checks(lib):
     r = lib.sce_refresh_e4m3_cache
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation

@@ -158,3 +158,61 @@ def test_host_build_feeds_the_step():
     assert torch.equal(dev["C"], db["C"]) and torch.equal(dev["aux"], db["aux"])
     for k in KEYS:
         assert torch.equal(got[k], ref[k]), k
+
+
+FP8_CASES = [
+    # T, d, V, P, prefix, stride
+    (300, 64, 1000, 333, True, 7),
+    (2050, 96, 2500, 1601, False, 3),
+    (1024, 16, 70000, 66000, True, 3),     # dW with more tiles than compute units
+    (16384, 768, 50304, 10240, False, 20011),
+]
+
+
+@pytest.mark.parametrize("T,d,V,P,prefix,stride", FP8_CASES)
+def test_fp8_prebuilt_equals_one_call_bitwise(T, d, V, P, prefix, stride):
+    """The e4m3 step from a device-built set, with the refreshed cache's scale read on the
+    device, equals the one-call e4m3 step bit for bit."""
+    print(f"fp8 prebuilt T={T} d={d} V={V} P={P}", flush=True)
+    x, W, y, p = _inputs(T + P + 3, T, d, V, "bf16", prefix)
+    cache = binding.refresh_e4m3_cache(W)
+    off = (T * 5) % V
+    ref = binding.forward_backward_fp8(x, cache["W8"], cache["w_scale"], y, p, P, stride, off,
+                                       want_rows=True)
+    cand = binding.build_candidates(y, p, V, P, stride, off)
+    got = binding.forward_backward_fp8_prebuilt(x, cache["W8"], cache["w_scale"], cand,
+                                                want_rows=True)
+    torch.cuda.synchronize()
+    for k in KEYS + ("scales",):
+        assert torch.equal(got[k], ref[k]), k
+    assert got["aux"][3].item() == 0
+
+
+def test_fp8_host_build_feeds_the_step():
+    """The page's arrangement end to end: candidate set built on the host, uploaded, the
+    e4m3 cache refreshed on the device, the e4m3 step from the uploaded set."""
+    T, d, V, P, stride, off = 2000, 128, 6000, 2500, 7, 123
+    x, W, y, p = _inputs(77, T, d, V, "bf16", True)
+    host = binding.build_candidates_host(y.cpu(), p.cpu(), V, P, stride, off)
+    cand = {k: (v.to(x.device) if v is not None else None) for k, v in host.items()}
+    cache = binding.refresh_e4m3_cache(W)
+    got = binding.forward_backward_fp8_prebuilt(x, cache["W8"], cache["w_scale"], cand,
+                                                want_rows=True)
+    ref = binding.forward_backward_fp8(x, cache["W8"], cache["w_scale"], y, p, P, stride, off,
+                                       want_rows=True)
+    torch.cuda.synchronize()
+    for k in KEYS + ("scales",):
+        assert torch.equal(got[k], ref[k]), k
+
+
+def test_fp8_prebuilt_bad_set_is_flagged():
+    T, d, V, P = 300, 64, 1000, 333
+    x, W, y, p = _inputs(78, T, d, V, "bf16", True)
+    cache = binding.refresh_e4m3_cache(W)
+    cand = binding.build_candidates(y, p, V, P, 7, 0)
+    C = cand["C"].clone()
+    C[5] = C[4]                          # not ascending
+    bad = dict(cand, C=C)
+    out = binding.forward_backward_fp8_prebuilt(x, cache["W8"], cache["w_scale"], bad)
+    torch.cuda.synchronize()
+    assert out["aux"][3].item() & binding.DEV_LABEL_RANGE
