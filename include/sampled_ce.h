@@ -196,9 +196,9 @@ SCE_API sce_status sampled_ce_forward_backward(const void* x, const void* W, con
  * beforehand. "sampled_softmax.py" (CandidateBuilder docstring, SampledSoftmax.prefetch /
  * upload / gather) builds the next microbatch's set off the step's critical path (on a
  * worker thread, then uploads it) and only gathers rows in the step. Here the results of
- * sce_build_candidates (or sce_build_candidates_noalloc) are the inputs, so a caller can
- * run the next microbatch's build on another stream, with its own workspace and output
- * arrays, while this step runs. The results are bit-identical to
+ * sce_build_candidates (or sce_build_candidates_noalloc, or sce_build_candidates_host
+ * uploaded to the device) are the inputs, so a caller can run the next microbatch's build
+ * on another stream or a host thread, with its own buffers, while this step runs. The results are bit-identical to
  * sampled_ce_forward_backward on the labels the set was built from.
  *
  *   x, W, T, d, V, dtype, loss, dX, dW, row_lse_out, row_loss_out: as in
