@@ -54,8 +54,10 @@ typedef enum sce_status {
   SCE_EHIP = 3        /* a HIP launch failed (see hipGetLastError) */
 } sce_status;
 
-/* SCE_E4M3 names the fp8 step (sampled_ce_forward_backward_fp8) in sce_workspace_size. */
-typedef enum sce_dtype { SCE_F32 = 0, SCE_BF16 = 1, SCE_E4M3 = 2 } sce_dtype;
+/* In sce_workspace_size: SCE_E4M3 names the fp8 steps that read an e4m3 cache
+ * (sampled_ce_forward_backward_fp8 and _fp8_prebuilt), SCE_E4M3_BF16W the fp8 step that
+ * encodes the candidate rows of bf16 weights itself (sampled_ce_forward_backward_fp8_bf16w). */
+typedef enum sce_dtype { SCE_F32 = 0, SCE_BF16 = 1, SCE_E4M3 = 2, SCE_E4M3_BF16W = 3 } sce_dtype;
 
 /* Device-detected conditions (bits of aux_out[3]). */
 #define SCE_DEV_TOO_MANY_TARGETS 1 /* distinct targets > P (the page asserts this never happens) */
@@ -284,6 +286,29 @@ SCE_API sce_status sampled_ce_forward_backward_fp8_prebuilt(
     const int64_t* build_aux, int64_t T, int64_t d, int64_t V, int64_t P, float* loss, void* dX,
     void* dW, float* row_lse_out, float* row_loss_out, int64_t* aux_out, float* scales_out,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sampled_ce_forward_backward_fp8_bf16w -- the e4m3 step from the bf16 weights, with the
+ * cache refresh folded in: the step reads only the candidate rows of the e4m3 lm_head
+ * cache ("sampled_softmax.py" refreshes the cache, then gathers those rows), so it forms
+ * the cache's scale and the codes of exactly those rows itself. max|W| is taken by spare
+ * workgroups beside the candidate build, and the row gather reads W[C] in bf16 and
+ * writes their codes under the rule of sce_refresh_e4m3_cache:
+ *   s_w = float32(max|W| / 448) (1 when W is all zeros), W8_C = e4m3(float32(W[C] / s_w)).
+ * The results equal, bit for bit, sce_refresh_e4m3_cache(W) followed by
+ * sampled_ce_forward_backward_fp8 with the refreshed cache and its device scale.
+ *   W [V, d] bf16 (the lm_head weights, 16-byte aligned); every other argument as in
+ *   sampled_ce_forward_backward_fp8, except:
+ *   scales_out [3] float32 or NULL: {s_x, s_g, s_w}.
+ *   workspace: at least sce_workspace_size(T, d, V, P, SCE_E4M3_BF16W) bytes.
+ * A non-finite W sets SCE_DEV_SCALE_RANGE (s_w is then 1).
+ */
+SCE_API sce_status sampled_ce_forward_backward_fp8_bf16w(
+    const void* x, const void* W, const int64_t* targets, const int64_t* prefix_targets, int64_t T,
+    int64_t d, int64_t V, int64_t P, int64_t stride, int64_t offset, float* loss, void* dX,
+    void* dW, int32_t* candidates_out, int32_t* target_pos_out, int32_t* prefix_pos_out,
+    float* row_lse_out, float* row_loss_out, int64_t* aux_out, float* scales_out, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * sce_refresh_e4m3_cache -- rebuilds the e4m3 lm_head cache the fp8 step reads from the

@@ -13,7 +13,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsampledce.so")
 
-SCE_F32, SCE_BF16, SCE_E4M3 = 0, 1, 2
+SCE_F32, SCE_BF16, SCE_E4M3, SCE_E4M3_BF16W = 0, 1, 2, 3
 DEV_TOO_MANY_TARGETS, DEV_LABEL_RANGE, DEV_SCALE_RANGE = 1, 2, 4
 # size limits (SCE_MAX_V_SAMPLED, SCE_MAX_V, SCE_MAX_D of include/sampled_ce.h)
 MAX_V_SAMPLED, MAX_V, MAX_D = 131072, 1048576, 16384
@@ -23,6 +23,7 @@ EXPORTS = ("sce_workspace_size", "sce_build_candidates", "sce_build_candidates_n
            "sce_build_candidates_host",
            "sampled_ce_forward_backward", "sampled_ce_forward_backward_prebuilt",
            "sampled_ce_forward_backward_fp8", "sampled_ce_forward_backward_fp8_prebuilt",
+           "sampled_ce_forward_backward_fp8_bf16w",
            "sce_refresh_e4m3_cache",
            "sce_ce_rows_workspace_size", "sce_ce_rows", "sce_gather_rows",
            "sce_profile_enable", "sce_profile_collect", "sce_status_string", "sce_abi_version")
@@ -70,6 +71,9 @@ def load_library(path: str = LIB_PATH):
                                                              i64, i64, i64, i64, p, p, p, p, p,
                                                              p, p, p, sz, p]
     lib.sampled_ce_forward_backward_fp8_prebuilt.restype = i32
+    lib.sampled_ce_forward_backward_fp8_bf16w.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                                          p, p, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.sampled_ce_forward_backward_fp8_bf16w.restype = i32
     lib.sce_refresh_e4m3_cache.argtypes = [p, i64, i64, p, p, p, p, sz, p]
     lib.sce_refresh_e4m3_cache.restype = i32
     lib.sce_ce_rows_workspace_size.argtypes = [i64, ctypes.POINTER(sz)]
@@ -464,6 +468,59 @@ def refresh_e4m3_cache(W, *, outputs=None, ws=None):
                                     _ptr(o["status"]), _ptr(ws), ws.numel(), _stream(dev))
     if rc != 0:
         raise SceError("sce_refresh_e4m3_cache", rc)
+    return o
+
+
+def forward_backward_fp8_bf16w(x, W, targets, prefix_targets, P, stride, offset, *,
+                               outputs=None, ws=None, want_rows=False):
+    """The e4m3 step from bf16 weights W [V, d], the cache refresh folded in (the scale
+    and the candidate rows' codes formed inside the step). Returns the keys of
+    forward_backward_fp8, with `scales` fp32 [3]: s_x, s_g, s_w."""
+    lib = load_library()
+    dev = x.device
+    T, d = x.shape
+    V = W.shape[0]
+    if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or W.shape[1] != d:
+        raise ValueError("x and W must be bf16 with the same hidden size")
+    for name, t in (("x", x), ("W", W), ("targets", targets)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if targets.dtype != torch.int64 or (prefix_targets is not None and prefix_targets.dtype != torch.int64):
+        raise ValueError("labels must be int64")
+    o = dict(outputs or {})
+    if "loss" not in o:
+        o["loss"] = torch.empty(1, dtype=torch.float32, device=dev)
+    if "dX" not in o:
+        o["dX"] = torch.empty_like(x)
+    if "dW" not in o:
+        o["dW"] = torch.empty(V, d, dtype=torch.bfloat16, device=dev)
+    if "C" not in o:
+        o["C"] = torch.empty(max(P, 1), dtype=torch.int32, device=dev) if P > 0 else None
+    for k in ("target_pos", "prefix_pos"):
+        if k not in o:
+            o[k] = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    if "aux" not in o:
+        o["aux"] = torch.empty(4, dtype=torch.int64, device=dev)
+    if "scales" not in o:
+        o["scales"] = torch.empty(3, dtype=torch.float32, device=dev)
+    if want_rows:
+        for k in ("row_lse", "row_loss"):
+            if k not in o:
+                o[k] = torch.empty(max(T, 1), dtype=torch.float32, device=dev)
+    nbytes = workspace_size(T, d, V, P, SCE_E4M3_BF16W)
+    if ws is None:
+        ws = workspace(nbytes, dev)
+    rc = lib.sampled_ce_forward_backward_fp8_bf16w(
+        _ptr(x), _ptr(W), _ptr(targets), _ptr(prefix_targets), T, d, V, P, stride, offset,
+        _ptr(o["loss"]), _ptr(o["dX"]), _ptr(o["dW"]), _ptr(o["C"]), _ptr(o["target_pos"]),
+        _ptr(o["prefix_pos"]), _ptr(o.get("row_lse")), _ptr(o.get("row_loss")), _ptr(o["aux"]),
+        _ptr(o["scales"]), _ptr(ws), ws.numel(), _stream(dev))
+    if rc != 0:
+        raise SceError("sampled_ce_forward_backward_fp8_bf16w", rc)
+    if o["C"] is not None:
+        o["C"] = o["C"][:P]
+    o["target_pos"] = o["target_pos"][:T]
+    o["prefix_pos"] = o["prefix_pos"][:T]
     return o
 
 

@@ -49,14 +49,17 @@ struct Plan {
 // full = false: only what the candidate build needs.
 Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full) {
   Plan p;
-  const bool e4m3 = dtype == SCE_E4M3;
+  // SCE_E4M3_BF16W: the e4m3 step that encodes the candidate rows of bf16 weights itself
+  // (every row at P == 0, into W_C)
+  const bool own_codes = dtype == SCE_E4M3_BF16W;
+  const bool e4m3 = dtype == SCE_E4M3 || own_codes;
   const size_t es = dtype == SCE_BF16 ? 2 : 4;  // logits element; the e4m3 step's are bf16
   const size_t ws = e4m3 ? 1 : es;              // W_C element
   p.Peff = P == 0 ? V : P;
   // e4m3 step: the gradient's rows share this pitch (a multiple of 16 bytes), and the
   // cross-entropy writes every column below it (zeros past P), so a product's 16-element
   // chunks that straddle K read zeros.
-  p.ldz = round_up(p.Peff, dtype == SCE_E4M3 ? 16 : 8);
+  p.ldz = round_up(p.Peff, e4m3 ? 16 : 8);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -74,7 +77,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bool full)
     // W_C rows are padded by 64 elements: with d * es a multiple of 512 bytes (d = 768
     // bf16: 1536 B), the logits product measured 15% slower on unpadded rows.
     p.ldwc = P > 0 ? d + 64 : d;
-    p.wc = take(P > 0 ? (size_t)P * p.ldwc * ws : 0);
+    p.wc = take(P > 0 || own_codes ? (size_t)p.Peff * p.ldwc * ws : 0);
     if (dtype == SCE_BF16) {
       // The dX product's B operand: W_C transposed (W itself at P = 0), k contiguous,
       // rows a multiple of 16 bytes with zeros past P_eff.
@@ -120,8 +123,9 @@ sce_status check_sizes(int64_t T, int64_t d, int64_t V, int64_t P, int dtype, bo
   if (P > 0 && V > SCE_MAX_V_SAMPLED) return SCE_EINVAL;
   if (need_d && (d < 8 || d % 8 != 0 || d > SCE_MAX_D)) return SCE_EINVAL;
   if (need_d && T * d > SCE_MAX_TD) return SCE_EINVAL;
-  if (dtype != SCE_F32 && dtype != SCE_BF16 && dtype != SCE_E4M3) return SCE_EINVAL;
-  if (dtype == SCE_E4M3 && need_d && d % 16 != 0) return SCE_EINVAL;
+  if (dtype != SCE_F32 && dtype != SCE_BF16 && dtype != SCE_E4M3 && dtype != SCE_E4M3_BF16W)
+    return SCE_EINVAL;
+  if ((dtype == SCE_E4M3 || dtype == SCE_E4M3_BF16W) && need_d && d % 16 != 0) return SCE_EINVAL;
   return SCE_OK;
 }
 
@@ -372,7 +376,7 @@ static hipError_t enqueue_products(const Plan& p, char* ws, const void* x, const
 static sce_status check_step(const void* x, const void* W, const void* labels, int64_t T,
                              int64_t d, int64_t V, int64_t P, int dtype, const float* loss,
                              const void* dX, const void* dW) {
-  if (dtype == SCE_E4M3) return SCE_EINVAL;  // sampled_ce_forward_backward_fp8
+  if (dtype == SCE_E4M3 || dtype == SCE_E4M3_BF16W) return SCE_EINVAL;  // the e4m3 entry points
   const sce_status st = check_sizes(T, d, V, P, dtype, true);
   if (st != SCE_OK) return st;
   if (W == nullptr || loss == nullptr || dW == nullptr) return SCE_EINVAL;
@@ -599,6 +603,54 @@ sce_status sampled_ce_forward_backward_fp8(const void* x, const void* W8, float 
   return hip_status(e);
 }
 
+sce_status sampled_ce_forward_backward_fp8_bf16w(
+    const void* x, const void* W, const int64_t* targets, const int64_t* prefix_targets, int64_t T,
+    int64_t d, int64_t V, int64_t P, int64_t stride, int64_t offset, float* loss, void* dX,
+    void* dW, int32_t* candidates_out, int32_t* target_pos_out, int32_t* prefix_pos_out,
+    float* row_lse_out, float* row_loss_out, int64_t* aux_out, float* scales_out, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  sce_status st = check_fp8(x, W, 1.f, nullptr, targets, T, d, V, P, loss, dX, dW);
+  if (st != SCE_OK) return st;
+  int64_t s = 1;
+  if (P > 0) {
+    s = mod64(stride, V);
+    if (gcd64(s, V) != 1) return SCE_EINVAL;
+  }
+  const Plan p = make_plan(T, d, V, P, SCE_E4M3_BF16W, true);
+  if (workspace == nullptr || workspace_bytes < p.total) return SCE_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SCE_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + p.counters);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + p.bits);
+  int32_t* wpre = reinterpret_cast<int32_t*>(ws + p.wpre);
+  int32_t* cand = candidates_out ? candidates_out : reinterpret_cast<int32_t*>(ws + p.cand);
+  int32_t* tpos = target_pos_out ? target_pos_out : reinterpret_cast<int32_t*>(ws + p.tpos);
+  int32_t* ppos = prefix_pos_out ? prefix_pos_out : reinterpret_cast<int32_t*>(ws + p.ppos);
+  float* row_loss = row_loss_out ? row_loss_out : reinterpret_cast<float*>(ws + p.row_loss);
+  float* scales = reinterpret_cast<float*>(ws + p.scales);
+
+  StageMarks marks(hs);
+  marks.mark(SCE_STAGE_CANDIDATES);
+  int amax_parts = 0;  // max|x| partials, and max|W| partials, taken beside the build
+  CacheEncode enc;
+  enc.scale_slot = scales + kScaleWCache;
+  enc.scale_out = scales_out ? scales_out + 2 : nullptr;
+  hipError_t e = launch_candidates(targets, prefix_targets, (int)T, (int)V, (int)P, (int)s,
+                                   (int)mod64(offset, V), counters, cand, bits, wpre, nullptr,
+                                   tpos, ppos, W, (int)(d * 2), ws + p.wc, (int)p.ldwc, dW,
+                                   (int)(d * 2), hs, x, T * d, &amax_parts, nullptr, 0, &enc);
+  // the products read the codes the gather wrote (every row at P == 0), with s_w as the
+  // cache's scale, read on the device
+  if (e == hipSuccess)
+    e = enqueue_products_fp8(p, ws, x, ws + p.wc, 1.f, scales + kScaleWCache, T, d, P,
+                             prefix_targets ? 2 : 1, counters, cand, tpos, ppos, row_loss,
+                             row_lse_out, loss, dX, dW, aux_out, scales_out, amax_parts, marks,
+                             hs);
+  return hip_status(e);
+}
+
 sce_status sampled_ce_forward_backward_fp8_prebuilt(
     const void* x, const void* W8, float w_scale, const float* w_scale_dev,
     const int32_t* candidates, const int32_t* target_pos, const int32_t* prefix_pos,
@@ -638,7 +690,7 @@ sce_status sampled_ce_forward_backward_fp8_prebuilt(
 sce_status sce_refresh_e4m3_cache(const void* W, int64_t V, int64_t d, void* W8_out,
                                   float* w_scale_out, int32_t* status_out, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  static_assert(kCounterWords * sizeof(int32_t) <= SCE_REFRESH_WORKSPACE_BYTES,
+  static_assert((kAmaxX + kAmaxSlots) * sizeof(int32_t) <= SCE_REFRESH_WORKSPACE_BYTES,
                 "the refresh's partial maxima fit its workspace");
   if (V < 1 || V > SCE_MAX_V || d < 16 || d > SCE_MAX_D || d % 16 != 0) return SCE_EINVAL;
   if (W == nullptr || W8_out == nullptr || w_scale_out == nullptr) return SCE_EINVAL;

@@ -49,11 +49,19 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
                                                         int32_t* __restrict__ wpre,
                                                         int32_t* __restrict__ counters,
                                                         const uint4* __restrict__ amax_x,
-                                                        int64_t amax_nvec) {
-  // Blocks past the first: the e4m3 step's max|x| (one partial each), which needs
-  // nothing from the build and runs beside it on the otherwise idle chip.
+                                                        int64_t amax_nvec, int x_parts,
+                                                        const uint4* __restrict__ amax_w,
+                                                        int64_t amax_w_nvec) {
+  // Blocks past the first: the e4m3 step's max|x| (x_parts blocks, one partial each),
+  // then, when the step encodes bf16 weights itself, max|W| (partials at kAmaxW). They
+  // need nothing from the build and run beside it on the otherwise idle chip.
   if (blockIdx.x > 0) {
-    amax_bf16_block(amax_x, amax_nvec, (int)blockIdx.x - 1, (int)gridDim.x - 1, counters);
+    const int b = (int)blockIdx.x - 1;
+    if (b < x_parts)
+      amax_bf16_block(amax_x, amax_nvec, b, x_parts, counters);
+    else
+      amax_bf16_block(amax_w, amax_w_nvec, b - x_parts, (int)gridDim.x - 1 - x_parts,
+                      counters + (kAmaxW - kAmaxX));
     return;
   }
   extern __shared__ uint32_t lds_words[];
@@ -244,7 +252,8 @@ __global__ __launch_bounds__(256) void k_remap_gather(
     const int32_t* __restrict__ C, int row_vecs, uint4* __restrict__ WC, int wc_vecs,
     int gather_blocks, uint4* __restrict__ dW, int dw_vecs, int zero_blocks,
     int32_t* __restrict__ vocab_pos, uint16_t* __restrict__ WT, int64_t ldt, int tr_x,
-    const int32_t* __restrict__ tpos_in, const int32_t* __restrict__ ppos_in) {
+    const int32_t* __restrict__ tpos_in, const int32_t* __restrict__ ppos_in, int enc_parts,
+    float* __restrict__ enc_slot, float* __restrict__ enc_out) {
   const int b = (int)blockIdx.x;
   if (b >= remap_blocks + gather_blocks + zero_blocks) {
     const int c = (b - remap_blocks - gather_blocks - zero_blocks) * 256 + (int)threadIdx.x;
@@ -257,6 +266,29 @@ __global__ __launch_bounds__(256) void k_remap_gather(
   }
   if ((int)blockIdx.x >= remap_blocks) {
     const int g = (int)blockIdx.x - remap_blocks;
+    if (enc_parts > 0) {
+      // the gather with encoding: s_w from the max|W| partials (each block forms it; the
+      // first publishes it), then the codes of the bf16 rows W[C] (every row at P == 0)
+      __shared__ uint32_t wmax[256 / kWave];
+      uint32_t amax = 0;
+      for (int i = threadIdx.x; i < enc_parts; i += 256)
+        amax = max(amax, (uint32_t)counters[kAmaxW + i]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, kWave));
+      if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = amax;
+      __syncthreads();
+      amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+      const bool finite = (amax >> 7) < 255;  // bf16 magnitude bits: exponent all ones
+      const float s_w = amax == 0 || !finite ? 1.f : bf16_to_f32((bf16_t)amax) / 448.f;
+      if (g == 0 && threadIdx.x == 0) {
+        *enc_slot = s_w;
+        if (enc_out) *enc_out = s_w;
+        if (!finite) atomicOr(&counters[kStatus], kDevScaleRange);
+      }
+      gather_encode_block(g, W, P > 0 ? C : nullptr, P > 0 ? P : V, row_vecs,
+                          reinterpret_cast<uint8_t*>(WC), (int64_t)wc_vecs * 16, s_w);
+      return;
+    }
     if (WT)
       transpose_tile<uint16_t>(g % tr_x, g / tr_x, reinterpret_cast<const uint16_t*>(W),
                                (int64_t)row_vecs * 8, C, P, row_vecs * 8, WT, ldt,
@@ -357,21 +389,30 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                              int32_t* prefix_pos, const void* W, int row_bytes, void* WC,
                              int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s,
                              const void* amax_x, int64_t amax_n, int* amax_parts, void* WT,
-                             int64_t ldt) {
+                             int64_t ldt, CacheEncode* enc) {
   const bool mark_lds = V <= kMaxBitmapClasses;
   const size_t lds = mark_lds ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
   const int agrid = amax_n >= 0 ? amax_block_count(amax_n / 8) : 0;
   if (amax_parts) *amax_parts = agrid;
-  hipLaunchKernelGGL(k_cand, dim3(1 + agrid), dim3(kBuildThreads), lds, s, targets, prefix, T, V,
-                     P, stride, off, mark_lds, C, bits, wpre, counters,
-                     static_cast<const uint4*>(amax_x), amax_n / 8);
+  // with enc: W holds bf16 rows of row_bytes; its max|W| partials come from more blocks
+  const int64_t w_nvec = enc ? (int64_t)V * (row_bytes / 16) : 0;
+  const int wgrid = enc ? amax_block_count(w_nvec) : 0;
+  if (enc) {
+    if (W == nullptr || WT != nullptr || enc->scale_slot == nullptr) return hipErrorInvalidValue;
+    enc->w_parts = wgrid;
+  }
+  hipLaunchKernelGGL(k_cand, dim3(1 + agrid + wgrid), dim3(kBuildThreads), lds, s, targets, prefix,
+                     T, V, P, stride, off, mark_lds, C, bits, wpre, counters,
+                     static_cast<const uint4*>(amax_x), amax_n / 8, agrid,
+                     static_cast<const uint4*>(enc ? W : nullptr), w_nvec);
   const int remap_blocks = (T + 255) / 256;
   // with WT: gather-and-transpose tiles, kTrTile rows of W_C by kTrTile of its columns
   const bool tr = WT != nullptr && W != nullptr && P > 0;
   const int tr_x = tr ? (int)((ldt + kTrTile - 1) / kTrTile) : 1;
   const int gather_blocks =
-      tr ? tr_x * ((row_bytes / 2 + kTrTile - 1) / kTrTile)
-         : ((W != nullptr && P > 0) ? gather_block_count(P, row_bytes / 16) : 0);
+      enc ? gather_block_count(P > 0 ? P : V, row_bytes / 16)
+      : tr ? tr_x * ((row_bytes / 2 + kTrTile - 1) / kTrTile)
+           : ((W != nullptr && P > 0) ? gather_block_count(P, row_bytes / 16) : 0);
   const int zero_blocks = (dW != nullptr && P > 0) ? zero_block_count(V, dw_row_bytes / 16) : 0;
   const int map_blocks = (vocab_pos != nullptr && P > 0) ? (V + 255) / 256 : 0;
   const int grid = remap_blocks + gather_blocks + zero_blocks + map_blocks;
@@ -381,7 +422,9 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                        reinterpret_cast<const uint4*>(W), C, row_bytes / 16,
                        reinterpret_cast<uint4*>(WC), wc_row_bytes / 16, gather_blocks,
                        reinterpret_cast<uint4*>(dW), dw_row_bytes / 16, zero_blocks, vocab_pos,
-                       static_cast<uint16_t*>(tr ? WT : nullptr), ldt, tr_x, nullptr, nullptr);
+                       static_cast<uint16_t*>(tr ? WT : nullptr), ldt, tr_x, nullptr, nullptr,
+                       enc ? enc->w_parts : 0, enc ? enc->scale_slot : nullptr,
+                       enc ? enc->scale_out : nullptr);
   return hipGetLastError();
 }
 
@@ -414,7 +457,7 @@ hipError_t launch_candidates_prebuilt(const int32_t* C_in, const int32_t* tpos_i
                        reinterpret_cast<uint4*>(WC), wc_row_bytes / 16, gather_blocks,
                        reinterpret_cast<uint4*>(dW), dw_row_bytes / 16, zero_blocks, nullptr,
                        static_cast<uint16_t*>(tr ? WT : nullptr), ldt, tr_x, tpos_in,
-                       T > 0 ? ppos_in : nullptr);
+                       T > 0 ? ppos_in : nullptr, 0, nullptr, nullptr);
   return hipGetLastError();
 }
 

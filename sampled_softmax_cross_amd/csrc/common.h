@@ -17,10 +17,12 @@ enum Counter : int {
   kCeDone = 4,     // CE rows finished (the last one reduces the loss)
   kNumCounters = 8,
   // After the counters (not cleared with them): the e4m3 step's bf16 magnitude bits of
-  // max|x|, one partial per workgroup of the amax launch (at most kAmaxSlots).
+  // max|x|, one partial per workgroup of the amax launch (at most kAmaxSlots), then
+  // those of max|W| when the step encodes the candidate rows of bf16 weights itself.
   kAmaxX = kNumCounters,
   kAmaxSlots = 1024,
-  kCounterWords = kAmaxX + kAmaxSlots
+  kAmaxW = kAmaxX + kAmaxSlots,
+  kCounterWords = kAmaxW + kAmaxSlots
 };
 constexpr int kDevTooManyTargets = 1;
 constexpr int kDevLabelRange = 2;
@@ -35,6 +37,7 @@ enum Scale : int {
   kScaleX = 3,       // s_x
   kScaleG = 4,       // s_g
   kScaleW = 5,       // w_scale
+  kScaleWCache = 6,  // s_w formed by the step from bf16 weights (read as a device w_scale)
   kNumScales = 8
 };
 

@@ -19,13 +19,26 @@ constexpr int kMaxBitmapClasses = 131072;
 // map. With amax_n >= 0 the build's launch also takes max|x| over amax_x (bf16, amax_n
 // elements, a multiple of 8; null when amax_n == 0) in *amax_parts partials
 // (counters[kAmaxX + i]) for launch_quant_x.
+// The e4m3 step's own encoding of bf16 weights (CacheEncode given to launch_candidates):
+// the build's launch also takes max|W| over W (bf16 [V, d], the `W` argument) in
+// w_parts partials (counters[kAmaxW + i]); the gather then reads the bf16 rows W[C]
+// (all V rows at P == 0) and writes their e4m3 codes e4m3(float32(W / s_w)),
+// s_w = float32(max|W| / 448) (1 for an all-zero or non-finite W; the latter also sets
+// kDevScaleRange), the rule of launch_refresh_e4m3, to W_C (rows of wc_row_bytes).
+// s_w goes to *scale_slot (and *scale_out when given).
+struct CacheEncode {
+  int w_parts = 0;              // set by launch_candidates
+  float* scale_slot = nullptr;  // device: s_w for the later kernels
+  float* scale_out = nullptr;   // device or null: the caller's copy of s_w
+};
 hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int T, int V, int P,
                              int stride, int off, int32_t* counters, int32_t* C, uint32_t* bits,
                              int32_t* wpre, int32_t* vocab_pos, int32_t* target_pos,
                              int32_t* prefix_pos, const void* W, int row_bytes, void* WC,
                              int wc_row_bytes, void* dW, int dw_row_bytes, hipStream_t s,
                              const void* amax_x = nullptr, int64_t amax_n = -1,
-                             int* amax_parts = nullptr, void* WT = nullptr, int64_t ldt = 0);
+                             int* amax_parts = nullptr, void* WT = nullptr, int64_t ldt = 0,
+                             CacheEncode* enc = nullptr);
 hipError_t launch_write_aux(const int32_t* counters, int64_t* aux, hipStream_t s);
 // The candidate stage for a set built beforehand (P > 0, V <= kMaxBitmapClasses): C_in
 // [P] ascending classes and the label positions tpos_in / ppos_in (ppos_in may be null)
@@ -72,6 +85,48 @@ __device__ __forceinline__ void gather_rows_block(int blk, const uint4* __restri
     if (k3) dst[v0 + 96] = b3;
   }
 }
+// e4m3 codes of 8 bf16 values over s_w: W / s_w correctly rounded (float division),
+// clamped to [-448, 448] (every value in [448, 464) encodes as 448, and s_w rounded below
+// max|W| / 448 can put the largest quotient a rounding error above 448), round to
+// nearest even.
+__device__ __forceinline__ uint2 encode_e4m3x8(const uint4& q, float s_w) {
+  auto quo = [s_w](float w) { return fminf(fmaxf(w / s_w, -448.f), 448.f); };
+  uint2 o;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(q.x << 16)),
+                                          quo(__uint_as_float(q.x & 0xffff0000u)), 0, false);
+  o.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(q.y << 16)),
+                                                  quo(__uint_as_float(q.y & 0xffff0000u)), w, true);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(q.z << 16)),
+                                      quo(__uint_as_float(q.z & 0xffff0000u)), 0, false);
+  o.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quo(__uint_as_float(q.w << 16)),
+                                                  quo(__uint_as_float(q.w & 0xffff0000u)), w, true);
+  return o;
+}
+// The gather with encoding: rows r of block blk (kGatherRows of them, 32 lanes each) read
+// bf16 row map ? map[r] : r of W (row_vecs 16-byte vectors) and write its e4m3 codes to
+// row r of WC (wc_bytes apart), every load of a lane issued before its stores.
+__device__ __forceinline__ void gather_encode_block(int blk, const uint4* __restrict__ W,
+                                                    const int32_t* __restrict__ map, int rows,
+                                                    int row_vecs, uint8_t* __restrict__ WC,
+                                                    int64_t wc_bytes, float s_w) {
+  const int r = blk * kGatherRows + (int)(threadIdx.x >> 5);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 31;
+  const uint4* src = W + (int64_t)(map ? map[r] : r) * row_vecs;
+  uint2* dst = reinterpret_cast<uint2*>(WC + (int64_t)r * wc_bytes);
+  for (int v0 = l; v0 < row_vecs; v0 += 32 * 4) {
+    uint4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = v0 + 32 * j;
+      q[j] = src[v < row_vecs ? v : v0];  // past the row: a vector it has (not stored)
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (v0 + 32 * j < row_vecs) dst[v0 + 32 * j] = encode_e4m3x8(q[j], s_w);
+  }
+}
+
 // Tiled transpose through LDS: one block of 256 lanes moves the kTrTile x kTrTile tile
 // (bx, by) of dst[c, r] = src[map ? map[r] : r, c] (r < rows, c < cols; dst columns r in
 // [rows, ld_dst) get zeros). It reads 16-byte chunks along the source rows and writes
@@ -201,8 +256,8 @@ hipError_t launch_quant_x(const void* x, int64_t n, int32_t* counters, float w_s
                           const float* w_scale_dev, void* x8, float* scales, float* scales_out,
                           hipStream_t s, int amax_parts = 0);
 // The e4m3 lm_head cache refresh: W8 = e4m3(W / s_w), s_w = max|W| / 448 (float32; 1 for an
-// all-zero W) written to *scale_out, over n bf16 values (a multiple of 8). part: kCounterWords
-// ints of scratch for the per-workgroup maxima; status (may be null) is set to 0, or to
+// all-zero W) written to *scale_out, over n bf16 values (a multiple of 8). part: kAmaxX +
+// kAmaxSlots ints of scratch for the per-workgroup maxima; status (may be null) is set to 0, or to
 // kDevScaleRange when W holds a non-finite value.
 hipError_t launch_refresh_e4m3(const void* W, int64_t n, void* W8, float* scale_out,
                                int32_t* status, int32_t* part, hipStream_t s);

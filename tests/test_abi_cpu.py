@@ -38,6 +38,11 @@ def test_binding_constants_match_the_header():
     assert binding.MAX_V == define("SCE_MAX_V")
     assert binding.MAX_D == define("SCE_MAX_D")
     assert binding.DEV_SCALE_RANGE == define("SCE_DEV_SCALE_RANGE")
+    enum = re.search(r"typedef enum sce_dtype \{([^}]*)\}", src).group(1)
+    codes = {k: int(v) for k, v in re.findall(r"(SCE_\w+)\s*=\s*(\d+)", enum)}
+    assert codes == {"SCE_F32": binding.SCE_F32, "SCE_BF16": binding.SCE_BF16,
+                     "SCE_E4M3": binding.SCE_E4M3, "SCE_E4M3_BF16W": binding.SCE_E4M3_BF16W}
+    assert binding.REFRESH_WORKSPACE_BYTES == define("SCE_REFRESH_WORKSPACE_BYTES")
 
 
 def test_version_and_status_strings(lib):
@@ -159,6 +164,39 @@ def test_fp8_host_checks(lib):
     assert g(fake, fake, fake, None, 4, 16, 16, 4, 3, 0, binding.SCE_E4M3, fake, fake, fake, None, None,
              None, None, None, None, None, 0, None) == 1  # the e4m3 step has its own entry point
 
+
+
+def test_fp8_bf16w_host_checks(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.sce_workspace_size(16384, 768, 50304, 10240, binding.SCE_E4M3_BF16W, ctypes.byref(out)) == 0
+    sampled = out.value
+    assert lib.sce_workspace_size(16384, 768, 50304, 10240, binding.SCE_E4M3, ctypes.byref(out)) == 0
+    assert sampled == out.value                          # the same plan when P > 0
+    assert lib.sce_workspace_size(4096, 768, 50304, 0, binding.SCE_E4M3_BF16W, ctypes.byref(out)) == 0
+    full_own = out.value
+    assert lib.sce_workspace_size(4096, 768, 50304, 0, binding.SCE_E4M3, ctypes.byref(out)) == 0
+    assert full_own >= out.value + 50304 * 768           # P = 0: room for every row's codes
+    assert lib.sce_workspace_size(16, 24, 100, 10, binding.SCE_E4M3_BF16W, ctypes.byref(out)) == 1
+    f = lib.sampled_ce_forward_backward_fp8_bf16w
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    args = dict(x=fake, W=fake, y=fake, p=None, T=4, d=16, V=16, P=4, stride=3, off=0, loss=fake,
+                dX=fake, dW=fake, c=None, tp=None, pp=None, lse=None, rl=None, aux=None, sc=None,
+                wsp=None, wsb=0, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    assert call() == 2                                   # no workspace
+    assert call(d=8) == 1                                # d % 16 != 0
+    assert call(stride=4) == 1                           # gcd(4, 16) != 1
+    assert call(W=None) == 1
+    assert call(W=ctypes.c_void_p((1 << 20) + 8)) == 1   # misaligned
+    assert call(y=None) == 1                             # T > 0 needs targets
+    assert call(wsp=fake, wsb=16) == 2                   # too small
+    g = lib.sampled_ce_forward_backward
+    assert g(fake, fake, fake, None, 4, 16, 16, 4, 3, 0, binding.SCE_E4M3_BF16W, fake, fake, fake,
+             None, None, None, None, None, None, None, 0, None) == 1  # its own entry point
 
 
 def test_fp8_prebuilt_host_checks(lib):

@@ -17,7 +17,7 @@ def _run(V, P, stride, offset, y, p):
     r = binding.build_candidates(labels_dev(y), labels_dev(p), V, P, stride, offset,
                                  want_vocab_pos=True)
     torch.cuda.synchronize()
-    return {k: (v.cpu().numpy() if v is not None else None) for k, v in r.items()}
+    return {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in r.items()}
 
 
 def _check(V, P, stride, offset, y, p):

@@ -24,10 +24,11 @@ def _call(fn, outs, ws):
     return fn(outputs=outs, ws=ws, want_rows=True)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "e4m3", "e4m3_refresh"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "e4m3", "e4m3_refresh", "e4m3_bf16w"])
 def test_captured_step_replays_bitwise(dtype):
     """e4m3_refresh: the cache refresh from bf16 W and the e4m3 step reading its scale on
-    the device, captured together."""
+    the device, captured together; e4m3_bf16w: the e4m3 step that encodes the candidate
+    rows of bf16 W itself."""
     print(f"graph capture {dtype}", flush=True)
     x, W, y, p, P = _inputs(dtype)
     T, d = x.shape
@@ -46,6 +47,10 @@ def test_captured_step_replays_bitwise(dtype):
             return binding.forward_backward_fp8(xd, cache["W8"], cache["w_scale"], yd, pd, P, 7, 3,
                                                 **kw)
         nbytes = binding.workspace_size(T, d, V, P, binding.SCE_E4M3)
+    elif dtype == "e4m3_bf16w":
+        Wd = to_dev(W, "bf16")
+        fn = lambda **kw: binding.forward_backward_fp8_bf16w(xd, Wd, yd, pd, P, 7, 3, **kw)
+        nbytes = binding.workspace_size(T, d, V, P, binding.SCE_E4M3_BF16W)
     elif dtype == "e4m3":
         codes, scale = fp8.e4m3_cache(synth.to_f64(W, "bf16"))
         W8 = torch.from_numpy(codes).cuda()

@@ -108,3 +108,55 @@ def test_step_reads_the_refreshed_scale_on_device():
     out = binding.forward_backward_fp8(xd, cache["W8"], bad, yd, pd, P, 7, 3)
     torch.cuda.synchronize()
     assert out["aux"][3].item() & binding.DEV_SCALE_RANGE
+
+
+BF16W_CASES = [
+    # T, d, V, P, prefix, stride
+    (300, 64, 1000, 333, True, 7),
+    (2050, 96, 2500, 1601, False, 3),
+    (257, 144, 777, 0, True, 1),               # full softmax: every row encoded, ragged V
+    (1024, 16, 70000, 66000, True, 3),         # dW with more tiles than compute units
+    (48, 64, 1048576, 0, True, 1),             # V = SCE_MAX_V, full softmax
+    (16384, 768, 50304, 10240, False, 20011),  # the stage-0/1 workload
+    (0, 64, 1000, 333, True, 7),               # no tokens
+]
+
+
+@pytest.mark.parametrize("T,d,V,P,prefix,stride", BF16W_CASES)
+def test_step_from_bf16_weights_equals_refresh_then_step(T, d, V, P, prefix, stride):
+    """The e4m3 step that encodes the candidate rows itself gives, bit for bit, what the
+    cache refresh followed by the e4m3 step with the refreshed scale gives."""
+    print(f"fp8 from bf16 W T={T} d={d} V={V} P={P}", flush=True)
+    x, W, y, p = synth.small_case(T + V + P + 9, max(T, 1), d, V, "bf16", prefix=prefix,
+                                  ignore_frac=0.05)
+    x, y = x[:T], y[:T]
+    p = None if p is None else p[:T]
+    xd, Wd, yd, pd = to_dev(x, "bf16"), to_dev(W, "bf16"), labels_dev(y), labels_dev(p)
+    off = (T * 7) % V
+    cache = binding.refresh_e4m3_cache(Wd)
+    ref = binding.forward_backward_fp8(xd, cache["W8"], cache["w_scale"], yd, pd, P, stride, off,
+                                       want_rows=True)
+    got = binding.forward_backward_fp8_bf16w(xd, Wd, yd, pd, P, stride, off, want_rows=True)
+    torch.cuda.synchronize()
+    keys = ["loss", "dX", "dW", "target_pos", "prefix_pos", "aux"] + (["row_lse", "row_loss"] if T else [])
+    if P > 0:
+        keys.append("C")
+    for k in keys:
+        a, b = got[k], ref[k]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), k
+    assert torch.equal(got["scales"][:2], ref["scales"]), "s_x, s_g"
+    assert got["scales"][2].item() == cache["w_scale"].item()
+    assert got["aux"][3].item() == 0
+
+
+def test_step_from_bf16_weights_flags_non_finite():
+    T, d, V, P = 300, 64, 1000, 333
+    x, W, y, p = synth.small_case(91, T, d, V, "bf16", prefix=True)
+    W[17, 3] = 0x7F80                                # +inf in bf16
+    out = binding.forward_backward_fp8_bf16w(to_dev(x, "bf16"), to_dev(W, "bf16"), labels_dev(y),
+                                             labels_dev(p), P, 7, 3)
+    torch.cuda.synchronize()
+    assert out["aux"][3].item() & binding.DEV_SCALE_RANGE
+    assert out["scales"][2].item() == 1.0
