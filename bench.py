@@ -370,6 +370,8 @@ def main():
                          "operand step on the same bf16 microbatch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the step with the candidate build overlapped on the host")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="time only the headline workload (not the other configurations the "
                          "metric names)")
@@ -428,7 +430,7 @@ def main():
                            "the full-cache refresh runs in the overlapped-build leg")
         log(f"[bench] e4m3 full-cache refresh (beside the step): {refresh}")
     pipelined = None
-    if w.P > 0:
+    if w.P > 0 and not args.no_overlap:
         pms = b.pipelined_ms(args.steps, args.warmup)
         pipelined = {"ms_per_step": round(pms, 5), "value": round(w.T / (pms * 1e-3), 1),
                      "how": "next microbatch's candidate set built on the host "
