@@ -104,7 +104,12 @@ __device__ __forceinline__ int km_index(int k, int ch) {
 // the lanes' chunk offsets are computed once and held in registers; otherwise they
 // are recomputed at every issue from an opaque lane id (a few integer operations per
 // instruction), which frees 2 * kN registers for tiles that would otherwise spill.
-template <int R, bool KMAJ, int NW, int SK, int EB, bool KEEP = true>
+// EXT: the clip along the operand's memory rows (tile rows r-major, k k-major) is the
+// buffer's extent, which leaves one 32-bit compare per chunk for the other axis, and the
+// wave index is uniform (LDS destinations in SGPRs); otherwise every chunk compares both
+// coordinates. Measured on the 256 x 256 tiles (logits, dW): 1-5% faster; on the dX tiles:
+// 2.5% slower at P = 24576, so they keep the per-chunk compares.
+template <int R, bool KMAJ, int NW, int SK, int EB, bool KEEP = true, bool EXT = false>
 struct DmaTile {
   static constexpr int CPR = SK * EB / 16;  // chunks per r-major row
   static constexpr int RB = R * EB;         // bytes per k-major row
@@ -112,11 +117,14 @@ struct DmaTile {
   static_assert((R * SK * EB) % (1024 * NW) == 0 && (CPR == 4 || CPR == 8) &&
                     (!KMAJ || RB % 256 == 0 || RB == 384 || (EB == 1 && (RB % 128 == 0 || RB == 192))),
                 "tile shape");
+  static_assert(KEEP || EXT, "recomputed offsets come with the extent clip");
   static constexpr int kN = R * SK * EB / (1024 * NW);  // DMA instructions per wave per stage
   int off[KEEP ? kN : 1];  // byte offset of the lane's chunk from the tile origin
-  int kr[KEEP ? kN : 1];   // (k << 16) | row of the lane's chunk, for the clip: k of the chunk
-                           // (r-major) or its row (k-major), and its row (r-major) or first column
-  int w;                   // index of this wave among the NW that fill the tile
+  // the chunk's coordinates for the clip: with EXT its k (r-major) or first column
+  // (k-major); otherwise (k << 16) | row (r-major) or (row << 16) | first column (k-major)
+  int kr[KEEP ? kN : 1];
+  int w;    // index of this wave among the NW that fill the tile
+  int ldb;  // bytes per operand row in memory (ld * EB)
   int64_t ld;
   // (k, r) of chunk i of this wave for lane `lane`
   __device__ __forceinline__ static void chunk(int wv, int i, int lane, int& k, int& r) {
@@ -132,22 +140,30 @@ struct DmaTile {
   __device__ __forceinline__ void init(int64_t ld_, int wave) {
     w = wave;
     ld = ld_;
+    ldb = (int)(ld_ * EB);
     if constexpr (KEEP) {
       const int lane = threadIdx.x & 63;
 #pragma unroll
       for (int i = 0; i < kN; ++i) {
         int k, r;
         chunk(w, i, lane, k, r);
-        kr[i] = (k << 16) | r;
+        kr[i] = EXT ? (KMAJ ? r : k) : ((k << 16) | r);
         off[i] = (int)((KMAJ ? (int64_t)k * ld + r : (int64_t)r * ld + k) * EB);
       }
     }
   }
   // base: address of tile element (0, 0) of this stage; rows_valid / k_valid clip the
-  // tile (a clipped chunk reads zeros).
+  // tile (a clipped chunk reads zeros). With EXT, a chunk of a memory row at or past the
+  // last valid one starts at or beyond the extent (every chunk lies within its row), and
+  // the extent never needs to reach past the tile's SK (k-major) or R (r-major) rows.
   __device__ __forceinline__ void issue(const void* base, int64_t rows_valid, int64_t k_valid,
                                         uint4* tile) const {
-    const rsrc_t rs = make_rsrc(base);
+    constexpr int kLines = KMAJ ? SK : R, kLim = KMAJ ? R : SK;
+    const int64_t lines = KMAJ ? k_valid : rows_valid, cv = KMAJ ? rows_valid : k_valid;
+    const int lc = lines <= 0 ? 0 : (lines >= kLines ? kLines : (int)lines);
+    const int lim = cv <= 0 ? 0 : (cv >= kLim ? kLim : (int)cv);
+    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                                        EXT ? lc * ldb : kOOB, 0x00020000);
     int lane = 0;
     if constexpr (!KEEP) {
       lane = threadIdx.x & 63;
@@ -155,18 +171,20 @@ struct DmaTile {
     }
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-      int o, kk, rr;
+      int o;
+      bool in;
       if constexpr (KEEP) {
         o = off[i];
-        kk = kr[i] >> 16;
-        rr = kr[i] & 0xffff;
+        in = EXT ? kr[i] < lim : ((kr[i] >> 16) < k_valid && (kr[i] & 0xffff) < rows_valid);
       } else {
+        int kk, rr;
         chunk(w, i, lane, kk, rr);
         o = (int)(KMAJ ? kk * (int)ld + rr : rr * (int)ld + kk) * EB;
+        in = (KMAJ ? rr : kk) < lim;
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (__attribute__((address_space(3))) void*)(tile + (w * kN + i) * 64), 16,
-          (kk < k_valid && rr < rows_valid) ? o : kOOB, 0, 0, 0);
+          in ? o : kOOB, 0, 0, 0);
     }
   }
 };
@@ -275,8 +293,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
     return lds + (NSB == NS ? i * (A_SLOT + B_SLOT) + A_SLOT : NS * A_SLOT + i * B_SLOT);
   };
 
+  // 256 x 256 tiles (logits, dW) clip their ring loads by the buffer extent (see DmaTile)
+  constexpr bool kExt = BM == BN;
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = kExt ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
   const int wm = wid / WGN, wn = wid % WGN;
   const int nbx = (int)((N + BN - 1) / BN), nby = (int)((M + BM - 1) / BM);
   const int ntiles = nbx * nby;
@@ -335,8 +355,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
   // are twice bf16's, and spilled registers would be reloaded with vector loads that
   // wait on the DMA queue (measured 1.3x slower dW at S2-late shapes)
   constexpr bool kKeepOffsets = EB == 2 || TM * TN < 8;
-  DmaTile<BM, A_KM, NW, SK, EB, kKeepOffsets> ta;
-  DmaTile<BN, B_KM, NW, SK, EB, kKeepOffsets> tb;
+  DmaTile<BM, A_KM, NW, SK, EB, kKeepOffsets, kExt> ta;
+  DmaTile<BN, B_KM, NW, SK, EB, kKeepOffsets, kExt> tb;
   const char* const Ab = static_cast<const char*>(A);
   const char* const Bb = static_cast<const char*>(B);
   ta.init(lda, wid);
@@ -362,14 +382,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
     const int64_t kv = ca.iu < my_units ? ca.c.ke - k0 : 0;
     ta.issue(Ab + (A_KM ? k0 * lda + ca.c.m0 : ca.c.m0 * lda + k0) * EB, M - ca.c.m0, kv,
              a_slot(slot_idx));
-    advance(ca);
   };
   auto issue_b = [&](int slot_idx) {
     const int64_t k0 = cb.c.kb + (int64_t)cb.is * SK;
     const int64_t kv = cb.iu < my_units ? cb.c.ke - k0 : 0;
     tb.issue(Bb + (B_KM ? k0 * ldb + cb.c.n0 : cb.c.n0 * ldb + k0) * EB, N - cb.c.n0, kv,
              b_slot(slot_idx));
-    advance(cb);
   };
   // With equal depths both operands of a stage go out together from one cursor, A then
   // B (the wait counts are symmetric then), which keeps the second cursor's registers
@@ -381,7 +399,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
              a_slot(slot_idx));
     tb.issue(Bb + (B_KM ? k0 * ldb + ca.c.n0 : ca.c.n0 * ldb + k0) * EB, N - ca.c.n0, kv,
              b_slot(slot_idx));
+  };
+  // The issue functions leave the cursors where they are; this moves them past what was
+  // issued (a unit change is a branch, so it goes after the MFMAs an issue shares a block
+  // with).
+  auto advance_issued = [&]() {
     advance(ca);
+    if constexpr (NSB != NS) advance(cb);
   };
 
   const int arow = wm * WM;  // wave's first row / column in the tile
@@ -421,6 +445,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
       if (kReads > pairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - pairs, 0);
     }
   };
+  // Products without pinned reads issue the freed slots' ring loads among the last k-step's
+  // MFMAs, one or two after each, so the matrix cores keep working while the loads issue
+  // (bf16 dW 3-5% faster than issuing them all before that k-step; the e4m3 fragments are
+  // twice as wide, and keeping both stages' fragments live at once there spills).
+  constexpr bool kIssueAmongMfma = EB == 2 && !IL;
+  constexpr int kDma = LA + LB;  // ring loads per wave per stage
+  auto interleave_issue = [&]() {
+#pragma unroll
+    for (int g = 0; g < kMfma; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      const int n = g < kDma % kMfma ? kDma / kMfma + 1 : kDma / kMfma;
+      if (n == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      else if (n == 2) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      else if (n == 3) __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);
+      else if (n >= 4) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+    }
+  };
 
   // Prologue: fill every slot (B then A per stage), wait for global stage 0, fetch its
   // first fragments.
@@ -428,9 +469,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
   for (int s = 0; s < NS; ++s) {
     if constexpr (NSB == NS) {
       issue_stage(s);
+      advance(ca);
     } else {
-      if (s < NSB) issue_b(s);
+      if (s < NSB) {
+        issue_b(s);
+        advance(cb);
+      }
       issue_a(s);
+      advance(ca);
     }
   }
   vm_wait<WAIT0>();
@@ -459,17 +505,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
       // g + NS (A).
       vm_wait<WAIT>();
       lds_barrier();
-      if constexpr (NSB == NS) {
-        issue_stage(g % NS);
-      } else {
-        issue_b(g % NSB);
-        issue_a(g % NS);
-      }
+      auto issue_freed = [&]() {
+        if constexpr (NSB == NS) {
+          issue_stage(g % NS);
+        } else {
+          issue_b(g % NSB);
+          issue_a(g % NS);
+        }
+      };
       // Last k-step of stage g, with the first reads of stage g + 1 in its shadow
       // (after the last stage these read a slot that is never used: in bounds, ignored).
-      read_frags(g + 1, 0, 0);
-      mfma_step((KS - 1) & 1);
-      interleave();
+      if constexpr (kIssueAmongMfma) {
+        read_frags(g + 1, 0, 0);
+        issue_freed();
+        mfma_step((KS - 1) & 1);
+        interleave_issue();
+        advance_issued();
+      } else {
+        issue_freed();
+        advance_issued();
+        read_frags(g + 1, 0, 0);
+        mfma_step((KS - 1) & 1);
+        interleave();
+      }
     }
     if constexpr (EB == 1) {
       const float sc = *scale;
