@@ -493,6 +493,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     for (int s = 0; s < cc.nk; ++s, ++g) {
+      // e4m3: the k-steps before the stage boundary at raised wave priority (products
+      // 0.5-1.5% faster); in bf16 it undoes the dW issue interleave (14% slower)
+      if constexpr (EB == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int q = 0; q + 1 < KS; ++q) {
         // k-step q of stage g, with the reads of its k-step q + 1 in its shadow.
@@ -500,6 +503,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void k_gemm_mfma(
         mfma_step(q & 1);
         interleave();
       }
+      if constexpr (EB == 1) __builtin_amdgcn_s_setprio(0);
       // Stage g + 1 becomes visible; the slots of stage g have no readers left (all
       // of their fragment sets are in registers), so they take stages g + NSB (B) and
       // g + NS (A).

@@ -264,7 +264,10 @@ hipError_t launch_refresh_e4m3(const void* W, int64_t n, void* W8, float* scale_
 
 // max|x| partial of one amax block (kBuildThreads lanes; block `b` of `nb`) over nvec
 // 16-byte bf16 vectors, written as the magnitude's bits to counters[kAmaxX + b].
-constexpr int kAmaxLoads = 8;
+// 16 loads per lane: max|x| and max|W| of the stage-0/1 e4m3 step (102 MB) take 392
+// blocks, one round beside the candidate build (8 loads: 782 blocks, 1.5 rounds, and a
+// candidate stage 2.3 us longer).
+constexpr int kAmaxLoads = 16;
 inline int amax_block_count(int64_t nvec) {
   const int64_t want = (nvec + (int64_t)kBuildThreads * kAmaxLoads - 1) / ((int64_t)kBuildThreads * kAmaxLoads);
   return (int)(want < 1 ? 1 : (want > kAmaxSlots ? kAmaxSlots : want));
