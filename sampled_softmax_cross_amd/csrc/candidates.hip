@@ -58,9 +58,9 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand(const int64_t* __restric
   if (blockIdx.x > 0) {
     const int b = (int)blockIdx.x - 1;
     if (b < x_parts)
-      amax_bf16_block(amax_x, amax_nvec, b, x_parts, counters);
+      amax_bf16_block<kAmaxLoadsBuild>(amax_x, amax_nvec, b, x_parts, counters);
     else
-      amax_bf16_block(amax_w, amax_w_nvec, b - x_parts, (int)gridDim.x - 1 - x_parts,
+      amax_bf16_block<kAmaxLoadsBuild>(amax_w, amax_w_nvec, b - x_parts, (int)gridDim.x - 1 - x_parts,
                       counters + (kAmaxW - kAmaxX));
     return;
   }
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_cand_prebuilt(
     const uint4* __restrict__ amax_x, int64_t amax_nvec) {
   // Blocks past the first: the e4m3 step's max|x| partials, as beside the device build.
   if (blockIdx.x > 0) {
-    amax_bf16_block(amax_x, amax_nvec, (int)blockIdx.x - 1, (int)gridDim.x - 1, counters);
+    amax_bf16_block<kAmaxLoadsBuild>(amax_x, amax_nvec, (int)blockIdx.x - 1, (int)gridDim.x - 1, counters);
     return;
   }
   extern __shared__ uint32_t mark[];
@@ -392,11 +392,11 @@ hipError_t launch_candidates(const int64_t* targets, const int64_t* prefix, int 
                              int64_t ldt, CacheEncode* enc) {
   const bool mark_lds = V <= kMaxBitmapClasses;
   const size_t lds = mark_lds ? (size_t)2 * ((V + 31) / 32) * sizeof(uint32_t) : 0;
-  const int agrid = amax_n >= 0 ? amax_block_count(amax_n / 8) : 0;
+  const int agrid = amax_n >= 0 ? amax_block_count<kAmaxLoadsBuild>(amax_n / 8) : 0;
   if (amax_parts) *amax_parts = agrid;
   // with enc: W holds bf16 rows of row_bytes; its max|W| partials come from more blocks
   const int64_t w_nvec = enc ? (int64_t)V * (row_bytes / 16) : 0;
-  const int wgrid = enc ? amax_block_count(w_nvec) : 0;
+  const int wgrid = enc ? amax_block_count<kAmaxLoadsBuild>(w_nvec) : 0;
   if (enc) {
     if (W == nullptr || WT != nullptr || enc->scale_slot == nullptr) return hipErrorInvalidValue;
     enc->w_parts = wgrid;
@@ -437,7 +437,7 @@ hipError_t launch_candidates_prebuilt(const int32_t* C_in, const int32_t* tpos_i
                                       const void* amax_x, int64_t amax_n, int* amax_parts) {
   if (P < 1 || V > kMaxBitmapClasses) return hipErrorInvalidValue;
   const size_t lds = (size_t)((V + 31) / 32) * sizeof(uint32_t);
-  const int agrid = amax_n >= 0 ? amax_block_count(amax_n / 8) : 0;
+  const int agrid = amax_n >= 0 ? amax_block_count<kAmaxLoadsBuild>(amax_n / 8) : 0;
   if (amax_parts) *amax_parts = agrid;
   hipLaunchKernelGGL(k_cand_prebuilt, dim3(1 + agrid), dim3(kBuildThreads), lds, s, C_in, V, P,
                      build_aux, counters, C, bits, static_cast<const uint4*>(amax_x), amax_n / 8);

@@ -263,13 +263,16 @@ hipError_t launch_refresh_e4m3(const void* W, int64_t n, void* W8, float* scale_
                                int32_t* status, int32_t* part, hipStream_t s);
 
 // max|x| partial of one amax block (kBuildThreads lanes; block `b` of `nb`) over nvec
-// 16-byte bf16 vectors, written as the magnitude's bits to counters[kAmaxX + b].
-// 16 loads per lane: max|x| and max|W| of the stage-0/1 e4m3 step (102 MB) take 392
-// blocks, one round beside the candidate build (8 loads: 782 blocks, 1.5 rounds, and a
-// candidate stage 2.3 us longer).
-constexpr int kAmaxLoads = 16;
+// 16-byte bf16 vectors, written as the magnitude's bits to counters[kAmaxX + b]. LOADS
+// vectors per lane and round. Beside the candidate build, 16 (kAmaxLoadsBuild): max|x|
+// and max|W| of the stage-0/1 e4m3 step (102 MB) take 392 blocks, one round beside the
+// build (8 loads: 782 blocks, 1.5 rounds, and a candidate stage 2.3 us longer). Alone
+// (the cache refresh), 8 (kAmaxLoads): max|W| in 589 blocks, 15.7 us on average against
+// 18.1 us in 295 blocks, which spread unevenly over 256 CUs.
+constexpr int kAmaxLoads = 8, kAmaxLoadsBuild = 16;
+template <int LOADS = kAmaxLoads>
 inline int amax_block_count(int64_t nvec) {
-  const int64_t want = (nvec + (int64_t)kBuildThreads * kAmaxLoads - 1) / ((int64_t)kBuildThreads * kAmaxLoads);
+  const int64_t want = (nvec + (int64_t)kBuildThreads * LOADS - 1) / ((int64_t)kBuildThreads * LOADS);
   return (int)(want < 1 ? 1 : (want > kAmaxSlots ? kAmaxSlots : want));
 }
 // Magnitude bits of the largest |x| of 8 bf16 values (bf16 magnitudes order like their
@@ -286,21 +289,22 @@ __device__ __forceinline__ uint32_t amax8(const uint4& q) {
 }
 // Each block writes the largest magnitude it saw to its own partial (no atomics:
 // atomics on one address serialise, one per workgroup of 512 measured 10.8 us for a
-// 25 MB tensor); kAmaxLoads loads in flight per lane, all issued before the first use.
+// 25 MB tensor); LOADS loads in flight per lane, all issued before the first use.
+template <int LOADS = kAmaxLoads>
 __device__ __forceinline__ void amax_bf16_block(const uint4* __restrict__ x, int64_t nvec, int b,
                                                 int nb, int32_t* __restrict__ counters) {
   __shared__ uint32_t wmax[kBuildThreads / 64];
   uint32_t m = 0;
   const int64_t stride = (int64_t)nb * kBuildThreads;
-  for (int64_t i0 = (int64_t)b * kBuildThreads + threadIdx.x; i0 < nvec; i0 += kAmaxLoads * stride) {
-    uint4 q[kAmaxLoads];
+  for (int64_t i0 = (int64_t)b * kBuildThreads + threadIdx.x; i0 < nvec; i0 += LOADS * stride) {
+    uint4 q[LOADS];
 #pragma unroll
-    for (int j = 0; j < kAmaxLoads; ++j) {
+    for (int j = 0; j < LOADS; ++j) {
       const int64_t i = i0 + j * stride;
       q[j] = x[i < nvec ? i : nvec - 1];  // past the end: the last vector again (no change)
     }
 #pragma unroll
-    for (int j = 0; j < kAmaxLoads; ++j) m = max(m, amax8(q[j]));
+    for (int j = 0; j < LOADS; ++j) m = max(m, amax8(q[j]));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
