@@ -345,7 +345,8 @@ class Bench:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             call()
-        gms = _time_ms(g.replay, reps=reps, warmup=3)
+        # the first replays after a capture run slower; warm up past them
+        gms = _time_ms(g.replay, reps=reps, warmup=20)
         del g
         return gms
 
@@ -417,7 +418,7 @@ def main():
     stages = stage_table(stage_ms, work, ptype)
     log("[bench] stages: " + json.dumps(stages))
     roof = roofline_of(w, stage_ms, work, ptype, e4m3)
-    gms = b.graph_ms(w.P, max(20, min(args.steps, 200)))
+    gms = b.graph_ms(w.P, max(100, min(args.steps, 200)))
     log(f"[bench] as a replayed HIP graph: {gms:.4f} ms/step ({w.T / gms * 1e3 / 1e6:.2f} M tokens/s)")
     ms, wall = b.timed(w.P, args.steps, args.warmup)
     b.check_status(w.P)
